@@ -1,0 +1,188 @@
+/*
+ * moonep.h -- C ABI of libmoonep.so: the balanced expert-parallel hot path of
+ * MoonEP (redundant-expert planning, zero-copy permute/unpermute, grouped
+ * SwiGLU expert GEMM, replica gradient reduction) on one AMD Instinct MI355X
+ * (gfx950).
+ *
+ * Pages cited (title, site):
+ *   [AT] "Moonshot AI Open-Sources MoonEP: A Perfectly Balanced Expert Parallelism
+ *        Library for MoE Training", aitrending.vip
+ *   [AL] "MoonshotAI/MoonEP", agentlenshq.com
+ *   [TD] "MoonEP balances AI experts in MoE models ...", twodots.gr
+ *   [TC] "The Busiest Rank Sets Your Step Time: Running MoonEP's Planning Code
+ *        Ourselves", thakicloud.com
+ *
+ * Model.  R expert-parallel ranks are emulated as R static partitions of one
+ * GPU's memory.  Rank r holds S tokens; each token routes to K distinct experts
+ * out of E; rank r is the home of experts [r*E/R, (r+1)*E/R).  Every rank serves
+ * exactly C = S*K (token, k) rows after planning [TD, summary; TC, Overview].
+ * The weight tensor of a projection has rows [0, E) = home experts and rows
+ * [E, E+B) = the rank's B prefetch slots [TD, memory contract; TC, Installation
+ * and integration].  Here the home rows live in one [E, ...] array and the
+ * slot rows of all ranks in one [R, B, ...] array.
+ *
+ * Conventions for every entry point.
+ *   - Pointers are device pointers unless stated otherwise; the caller owns and
+ *     allocates every buffer; the library allocates nothing and keeps no state
+ *     between calls besides loaded kernels.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *     enqueues work on it and returns; nothing synchronises the host (the
+ *     static shapes make that possible [TD, architecture; TC, "What the
+ *     technique is"]).
+ *   - Layouts are dense row-major.  bf16 tensors are raw 16-bit bfloat16.
+ *   - Return value: MOONEP_OK, or a negative code detected on the host before
+ *     anything is enqueued (bad dims, NULL or misaligned pointer), or
+ *     MOONEP_EHIP if a launch failed.  Problems in the routing data itself are
+ *     found on the device and reported in stats[0] (bits MOONEP_ST_*), with no
+ *     host synchronisation.
+ *   - Device pointers must be 16-byte aligned; row sizes (H and I elements)
+ *     must be multiples of 8.
+ */
+#ifndef MOONEP_H
+#define MOONEP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct moonep_dims {
+    int32_t R;       /* emulated EP ranks, 1..64                                   */
+    int32_t E;       /* routed experts, multiple of R, E/R <= 64, E <= 1024         */
+    int32_t B;       /* prefetch slots per rank, 0..64                              */
+    int32_t S;       /* tokens per rank, >= 1                                       */
+    int32_t K;       /* experts per token, 1..min(E, 16)                            */
+    int32_t H;       /* hidden size, multiple of 8                                  */
+    int32_t I;       /* SwiGLU intermediate size, multiple of 8 (0 if no expert FFN) */
+    uint32_t flags;  /* MOONEP_TRAINING | MOONEP_F32_ROWS                          */
+} moonep_dims_t;
+
+#define MOONEP_TRAINING 1u   /* plan for training: a fallback replica sets MOONEP_ST_TRAIN_FALLBACK */
+#define MOONEP_F32_ROWS 2u   /* dispatch/combine rows are float32 instead of bf16 */
+
+enum {
+    MOONEP_OK = 0,
+    MOONEP_EINVAL = -1,   /* bad dims or NULL pointer       */
+    MOONEP_EALIGN = -2,   /* pointer not 16-byte aligned    */
+    MOONEP_EHIP = -3,     /* a HIP launch failed            */
+    MOONEP_ENOTSUP = -4   /* combination not supported      */
+};
+
+/* Device-detected routing problems, OR-ed into stats[0]. */
+#define MOONEP_ST_BAD_ID 1          /* an expert id outside [0, E): no plan made        */
+#define MOONEP_ST_DUP_ID 2          /* a token names one expert twice: no plan made     */
+#define MOONEP_ST_CAPACITY 4        /* some rank does not total S*K rows (never for a valid plan) */
+#define MOONEP_ST_OVERFLOW 8        /* plan entry table overflow (never for a valid plan)         */
+#define MOONEP_ST_TRAIN_FALLBACK 16 /* training plan has replicas beyond the B slots (informational) */
+
+/* stats[16] int32 written by moonep_plan:
+ *  0 status bits            1 replicas (plan entries)   2 replicas in prefetch slots
+ *  3 fallback replicas      4 fallback rows             5 migrated rows (sum of replica rows)
+ *  6 migration lower bound: sum over ranks of max(0, P[q] - S*K)
+ *  7 max per-expert load    8 max rows routed to one home rank (before planning)
+ *  9 min rows routed to one home rank   10 donor ranks   11 receiver ranks
+ * 12 max replicas on one rank           13 total planned rows (= R*S*K)   14, 15 zero
+ * Replicas are [TC, What we measured, Table 1]'s "copy slots"; migrated rows its
+ * "migrated tokens". */
+#define MOONEP_NSTATS 16
+
+/* Bytes of the opaque device workspace that moonep_plan fills and the other
+ * entry points read.  Pure host function.  Returns 0 for invalid dims. */
+size_t moonep_plan_workspace_bytes(const moonep_dims_t* dims);
+
+/* Online redundant-expert planning [TC, "What the technique is" flowchart:
+ * router output -> planning kernel; AL, How it works; TD, memory contract].
+ *   topk       [R, S, K] int32  expert ids chosen by the router for each token (k order kept)
+ *   plan_ws    workspace of moonep_plan_workspace_bytes() bytes; stays valid (and is read by
+ *              prefetch / grouped_ffn / reduce_grad) until the next moonep_plan on it
+ *   cu_seqlens [R, E+B+1] int32 out: per rank, prefix sums of the rows served by each weight
+ *              row (home rows [0,E), slot rows [E,E+B)); cu_seqlens[q][E+B] == S*K
+ *   dest       [R, S, K] int32 out: absolute row in the [R*S*K] receive buffer where the
+ *              (token, k) row goes, computed on the send side (zero-copy permute
+ *              [TC, "What the technique is"]); -1 when no plan was made
+ *   stats      [16] int32 out (see above)
+ * The plan follows a fixed deterministic rule (each rank's duplicates come from at most one
+ * other rank's home group [TC, Installation and integration]; replicas beyond the B slots
+ * read the home row, "fallback" [TD, memory contract]); results are bit-identical run to run. */
+int moonep_plan(const moonep_dims_t* dims, const int32_t* topk, void* plan_ws,
+                int32_t* cu_seqlens, int32_t* dest, int32_t* stats, void* stream);
+
+/* Weight prefetch [TC, flowchart "Weight prefetch"; TD, memory contract]: for every replica
+ * that got slot j on rank q, copy the home expert's weights into that slot.
+ *   w13_home [E, H, 2I] bf16 (gate | up columns), w2_home [E, I, H] bf16
+ *   w13_slot [R, B, H, 2I] bf16 out, w2_slot [R, B, I, H] bf16 out (unused slots untouched) */
+int moonep_prefetch(const moonep_dims_t* dims, const void* plan_ws,
+                    const void* w13_home, const void* w2_home,
+                    void* w13_slot, void* w2_slot, void* stream);
+
+/* Fused zero-copy permute [TC, "What the technique is"; AL, How it works; TD, architecture]:
+ * recv[dest[r,s,k]] = src[r,s] for every (token, k).
+ *   src  [R, S, H] bf16 (float32 with MOONEP_F32_ROWS)
+ *   row_scale [R, S, K] float32 or NULL.  NULL: bitwise copy.  Otherwise each copy is
+ *        multiplied by its scale in float32 and rounded to nearest even (the backward of a
+ *        gate-weighted combine).
+ *   recv [R*S*K, H] out, same element type as src.  Rows whose dest is -1 are skipped. */
+int moonep_dispatch(const moonep_dims_t* dims, const int32_t* dest, const void* src,
+                    const float* row_scale, void* recv, void* stream);
+
+/* Fused unpermute [TC, flowchart "combine"]: out[r,s] = sum over k (in k order, float32
+ * accumulation) of gates[r,s,k] * y[dest[r,s,k]], rounded to nearest even.
+ *   y     [R*S*K, H] bf16 (float32 with MOONEP_F32_ROWS)
+ *   gates [R, S, K] float32, or NULL for unit weights (the backward of dispatch)
+ *   out   [R, S, H] out, same element type as y. */
+int moonep_combine(const moonep_dims_t* dims, const int32_t* dest, const void* y,
+                   const float* gates, void* out, void* stream);
+
+/* Grouped SwiGLU expert FFN over the receive buffer [TC, flowchart "Group GEMM"; TD, memory
+ * contract: cu_seqlens selects the active weight rows].  For each group (rank q, weight row w)
+ * with rows X_g:  [Gt U] = X_g W13[w];  A = silu(Gt) * U;  Y_g = A W2[w]; bf16 inputs, float32
+ * accumulation, bf16 outputs.  Weight row w < E reads w13_home/w2_home[w] (home expert, or a
+ * fallback replica reading the home row); w >= E reads slot (q, w-E).
+ *   recv    [R*S*K, H] bf16
+ *   gu_save [R*S*K, 2I] bf16 out (Gt | U, kept for the backward) or NULL
+ *   act     [R*S*K, I] bf16 out
+ *   y       [R*S*K, H] bf16 out */
+int moonep_grouped_ffn(const moonep_dims_t* dims, const void* plan_ws, const int32_t* cu_seqlens,
+                       const void* recv, const void* w13_home, const void* w2_home,
+                       const void* w13_slot, const void* w2_slot,
+                       void* gu_save, void* act, void* y, void* stream);
+
+/* Backward of moonep_grouped_ffn.  dA = dY W2^T; dGt = dA U sig(Gt)(1 + Gt(1 - sig(Gt)));
+ * dU = dA silu(Gt); dX = [dGt dU] W13^T; dW2 = A^T dY; dW13 = X^T [dGt dU].
+ * Weight gradients of slot replicas go to the separate fp32 reduce buffers (they must not
+ * reach the framework's gradient reduction [TD, memory contract; AT, Technical Details]);
+ * home experts accumulate into dw*_home.  A fallback replica (training with B < E/R, an
+ * extension: the pages ask for B = E/R in training) accumulates into its home expert's
+ * gradient together with the home rows.
+ *   dy        [R*S*K, H] bf16 upstream gradient of y (e.g. moonep_dispatch with row_scale)
+ *   drecv     [R*S*K, H] bf16 out
+ *   dw13_home [E, H, 2I] float32, dw2_home [E, I, H] float32: accumulated (+=)
+ *   dw13_red  [R, B, H, 2I] float32, dw2_red [R, B, I, H] float32: accumulated (+=); the
+ *             slots are zero at the start of a step (moonep_reduce_grad clears them) */
+int moonep_grouped_ffn_backward(const moonep_dims_t* dims, const void* plan_ws,
+                                const int32_t* cu_seqlens, const void* recv,
+                                const void* gu_save, const void* act, const void* dy,
+                                const void* w13_home, const void* w2_home,
+                                const void* w13_slot, const void* w2_slot,
+                                void* drecv, float* dw13_home, float* dw2_home,
+                                float* dw13_red, float* dw2_red, void* stream);
+
+/* reduce_grad [TD, memory contract; AT, Technical Details]: for every expert, add its slot
+ * replicas' reduce-buffer gradients (in replica creation order) into the home gradient, then
+ * zero those slots for the next micro-batch.  Float32, in place. */
+int moonep_reduce_grad(const moonep_dims_t* dims, const void* plan_ws,
+                       float* dw13_home, float* dw2_home, float* dw13_red, float* dw2_red,
+                       void* stream);
+
+/* Static description of an error code. */
+const char* moonep_strerror(int code);
+
+/* Library version string. */
+const char* moonep_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOONEP_H */

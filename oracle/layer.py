@@ -255,8 +255,11 @@ def moe_direct(x, topk, gates, w13, w2) -> np.ndarray:
     return out
 
 
-def moe_direct_backward(x, topk, gates, w13, w2, dout):
-    """Gradients of ``moe_direct`` w.r.t. x, W13 and W2 for upstream dOut (float64)."""
+def moe_direct_backward(x, topk, gates, w13, w2, dout, experts=None):
+    """Gradients of ``moe_direct`` w.r.t. x, W13 and W2 for upstream dOut (float64).
+
+    ``experts`` restricts the computation to those experts (dx then only holds their share).
+    """
     xf = _f64(x)
     do = _f64(dout)
     R, S, H = xf.shape
@@ -266,7 +269,7 @@ def moe_direct_backward(x, topk, gates, w13, w2, dout):
     dW13 = np.zeros((E, H, 2 * I))
     dW2 = np.zeros((E, I, H))
     gf = np.asarray(gates, np.float64)
-    for e in range(E):
+    for e in (range(E) if experts is None else experts):
         r_i, s_i, k_i = np.nonzero(topk == e)
         if r_i.size == 0:
             continue

@@ -1,0 +1,252 @@
+"""GPU parity of weight prefetch, the grouped SwiGLU GEMM (forward and backward) and
+reduce_grad against the CPU oracle.
+
+Tolerance: relative Frobenius error <= 2e-2 for GEMM outputs and gradients (bf16
+inputs and outputs, fp32 accumulation, against a float64 oracle); prefetched slots
+and the permuted rows are bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import balanced_token_dispatch_moonep_amd as M
+from balanced_token_dispatch_moonep_amd.layer import MoonEPLayer
+import oracle as O
+import workload as W
+
+from gpu_util import (DEV, say, dims_of, i32, f32, bf16_from_bits, bits_of, f64_of,
+                      assert_plan_parity, rel_fro, max_row_rel)
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+
+# several 256x256 tiles per group with ragged tails; I = 320 is not a multiple of 128,
+# so the gate/up column tiles and the dA / dW column tiles are partial too
+MID = W.Config("mid", R=4, E=16, B=4, S=512, K=4, H=512, I=320, dtype="bf16", lam=1.0, seed=2)
+
+
+def _setup(cfg, B=None, training=False):
+    topk, gates, _ = W.routing_for(cfg)
+    xb = W.hidden_rows(cfg.R, cfg.S, cfg.H, cfg.seed, "bf16")
+    w13f, w2f = W.expert_weights_np(cfg.E, cfg.H, cfg.I, cfg.seed)
+    wb13, wb2 = W.bf16_bits(w13f), W.bf16_bits(w2f)
+    d = dims_of(cfg, B=B, training=training, f32_rows=False)
+    plan, dest, _ = assert_plan_parity(d, topk, training=training)
+    layer = MoonEPLayer(d, w13=bf16_from_bits(wb13), w2=bf16_from_bits(wb2), training=training)
+    return topk, gates, xb, wb13, wb2, d, plan, dest, layer
+
+
+@pytest.mark.parametrize("B", [4, 2, 0])
+def test_forward_mid(B):
+    cfg = MID.with_(B=B)
+    topk, gates, xb, wb13, wb2, d, plan, dest, layer = _setup(cfg)
+    say("forward mid B", B, "replicas", len(plan.entries),
+        "fallback", sum(1 for e in plan.entries if e.w < cfg.E))
+    out = layer.forward(bf16_from_bits(xb), i32(topk), f32(gates))
+    torch.cuda.synchronize()
+    recv = O.dispatch(dest, xb)
+    assert bits_of(layer.recv).tobytes() == recv.tobytes()
+    s13, s2 = O.prefetch(plan, wb13, wb2)
+    if B:
+        for en in plan.entries:
+            if en.w >= cfg.E:
+                assert np.array_equal(bits_of(layer.w13_slot[en.q, en.j]), s13[en.q, en.j])
+                assert np.array_equal(bits_of(layer.w2_slot[en.q, en.j]), s2[en.q, en.j])
+    gu, act, y = O.ffn_forward(plan, recv, wb13, wb2, s13, s2)
+    for name, got, ref in (("gu", layer.gu, gu), ("act", layer.act, act), ("y", layer.y, y)):
+        e = rel_fro(f64_of(got), ref)
+        say(f"  {name} rel fro {e:.3e}")
+        assert e <= TOL
+    for (q, w, row0, rows, kind, idx) in O.groups(plan):
+        assert rel_fro(f64_of(layer.y[row0:row0 + rows]), y[row0:row0 + rows]) <= TOL, (q, w, kind)
+    ref = O.combine(dest, y, gates)
+    assert max_row_rel(f64_of(out), ref) <= TOL
+    # the plan-free definition (duplicates and fallback do not change the result)
+    direct = O.moe_direct(xb, topk, gates, wb13, wb2)
+    e = rel_fro(f64_of(out), direct)
+    say(f"  out vs direct rel fro {e:.3e}")
+    assert e <= TOL
+
+
+def test_forward_deterministic():
+    topk, gates, xb, wb13, wb2, d, plan, dest, layer = _setup(MID)
+    x, tk, g = bf16_from_bits(xb), i32(topk), f32(gates)
+    first = layer.forward(x, tk, g).clone()
+    y1 = layer.y.clone()
+    for _ in range(2):
+        assert torch.equal(layer.forward(x, tk, g).view(torch.int16), first.view(torch.int16))
+        assert torch.equal(layer.y.view(torch.int16), y1.view(torch.int16))
+
+
+@pytest.mark.parametrize("B", [4, 2, 0])
+def test_backward_mid(B):
+    cfg = MID.with_(B=B)
+    topk, gates, xb, wb13, wb2, d, plan, dest, layer = _setup(cfg, training=True)
+    say("backward mid B", B)
+    dout = W.grad_rows(cfg.R, cfg.S, cfg.H, cfg.seed, "bf16")
+    layer.forward(bf16_from_bits(xb), i32(topk), f32(gates))
+    dx = layer.backward(bf16_from_bits(dout), f32(gates))
+    torch.cuda.synchronize()
+    recv = O.dispatch(dest, xb)
+    s13, s2 = O.prefetch(plan, wb13, wb2)
+    gu, act, y = O.ffn_forward(plan, recv, wb13, wb2, s13, s2)
+    dy = O.dispatch(dest, dout, row_scale=gates)
+    drecv, dW13, dW2, rb13, rb2 = O.ffn_backward(plan, recv, gu, act, dy, wb13, wb2, s13, s2)
+    e = rel_fro(f64_of(layer.drecv), drecv)
+    say(f"  drecv rel fro {e:.3e}")
+    assert e <= TOL
+    dx_ref = O.combine(dest, drecv, None)
+    assert rel_fro(f64_of(dx), dx_ref) <= TOL
+    O.reduce_grad(plan, dW13, dW2, rb13, rb2)
+    g13, g2 = f64_of(layer.dw13), f64_of(layer.dw2)
+    e13, e2 = rel_fro(g13, dW13), rel_fro(g2, dW2)
+    say(f"  dW13 rel fro {e13:.3e}  dW2 rel fro {e2:.3e}")
+    assert e13 <= TOL and e2 <= TOL
+    for ex in range(cfg.E):
+        if plan.L[ex] > 0:
+            assert rel_fro(g13[ex], dW13[ex]) <= TOL, ex
+            assert rel_fro(g2[ex], dW2[ex]) <= TOL, ex
+        else:
+            assert not g13[ex].any() and not g2[ex].any()
+    if B:
+        assert not layer.dw13_red.any() and not layer.dw2_red.any()
+    # plan-free gradients
+    rdx, rdW13, rdW2 = O.moe_direct_backward(xb, topk, gates, wb13, wb2, dout)
+    assert rel_fro(f64_of(dx), rdx) <= TOL
+    assert rel_fro(g13, rdW13) <= TOL and rel_fro(g2, rdW2) <= TOL
+
+
+def test_backward_accumulates():
+    """Two backward passes on the same batch double the home gradients; reduce buffers stay clean."""
+    topk, gates, xb, wb13, wb2, d, plan, dest, layer = _setup(MID, training=True)
+    dout = bf16_from_bits(W.grad_rows(MID.R, MID.S, MID.H, 7, "bf16"))
+    x, tk, g = bf16_from_bits(xb), i32(topk), f32(gates)
+    layer.forward(x, tk, g)
+    layer.backward(dout, g)
+    one13 = layer.dw13.clone()
+    layer.forward(x, tk, g)
+    layer.backward(dout, g)
+    torch.cuda.synchronize()
+    assert rel_fro(f64_of(layer.dw13), 2 * f64_of(one13)) <= 1e-6
+    assert not layer.dw13_red.any()
+
+
+def test_tiny_layer_f32_rows():
+    """Tiny configuration: fp32 token rows for dispatch/combine, bf16 expert GEMM."""
+    cfg = W.CONFIGS["tiny"]
+    topk, gates, _ = W.routing_for(cfg)
+    x = W.hidden_rows(cfg.R, cfg.S, cfg.H, cfg.seed, "f32")
+    w13f, w2f = W.expert_weights_np(cfg.E, cfg.H, cfg.I, cfg.seed)
+    wb13, wb2 = W.bf16_bits(w13f), W.bf16_bits(w2f)
+    d32 = dims_of(cfg, f32_rows=True)
+    dbf = dims_of(cfg, f32_rows=False)
+    plan, dest, (ws, cu, dd, st) = assert_plan_parity(d32, topk)
+    recv32 = torch.empty((cfg.R * cfg.C, cfg.H), dtype=torch.float32, device=DEV)
+    M.moonep_dispatch(d32, dd, f32(x), None, recv32)
+    recv = recv32.to(torch.bfloat16)                  # cast at the bf16 GEMM boundary
+    w13, w2 = bf16_from_bits(wb13), bf16_from_bits(wb2)
+    s13 = torch.zeros((cfg.R, cfg.B, cfg.H, 2 * cfg.I), dtype=torch.bfloat16, device=DEV)
+    s2 = torch.zeros((cfg.R, cfg.B, cfg.I, cfg.H), dtype=torch.bfloat16, device=DEV)
+    M.moonep_prefetch(dbf, ws, w13, w2, s13, s2)
+    nrows = cfg.R * cfg.C
+    act = torch.empty((nrows, cfg.I), dtype=torch.bfloat16, device=DEV)
+    y = torch.empty((nrows, cfg.H), dtype=torch.bfloat16, device=DEV)
+    M.moonep_grouped_ffn(dbf, ws, cu, recv, w13, w2, s13, s2, None, act, y)
+    y32 = y.float()
+    out = torch.empty((cfg.R, cfg.S, cfg.H), dtype=torch.float32, device=DEV)
+    M.moonep_combine(d32, dd, y32, f32(gates), out)
+    torch.cuda.synchronize()
+    assert recv32.cpu().numpy().tobytes() == O.dispatch(dest, x).tobytes()
+    direct = O.moe_direct(x, topk, gates, w13f, w2f)
+    e = rel_fro(f64_of(out), direct)
+    say(f"tiny layer out vs fp32-weight direct rel fro {e:.3e}")
+    assert e <= TOL
+
+
+# ----------------------------------------------------------------------------
+# full-size layer, sampled rows
+# ----------------------------------------------------------------------------
+
+def _full_layer(cfg, B, training):
+    topk, gates, lam = W.routing_for(cfg)
+    d = dims_of(cfg, B=B, training=training)
+    plan, dest, _ = assert_plan_parity(d, topk, training=training)
+    say("full layer maxvio", cfg.maxvio, "B", B, "replicas", len(plan.entries),
+        "fallback", sum(1 for e in plan.entries if e.w < cfg.E))
+    w13, w2 = W.expert_weights_torch(cfg.E, cfg.H, cfg.I, cfg.seed, DEV)
+    xb = W.hidden_rows(cfg.R, cfg.S, cfg.H, cfg.seed, "bf16")
+    layer = MoonEPLayer(d, w13=w13, w2=w2, training=training)
+    return topk, gates, xb, plan, dest, layer
+
+
+def _expert_np(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("B", [4, 3])
+def test_full_layer_forward_sampled(B):
+    cfg = W.CONFIGS["layer"]
+    topk, gates, xb, plan, dest, layer = _full_layer(cfg, B, False)
+    layer.forward(bf16_from_bits(xb), i32(topk), f32(gates))
+    torch.cuda.synchronize()
+    grp = O.groups(plan)
+    rng = np.random.default_rng(1)
+    kinds = {"home": [g for g in grp if g[4] == "home"], "slot": [g for g in grp if g[4] == "slot"],
+             "fallback": [g for g in grp if g[4] == "fallback"]}
+    picks = []
+    for kind, lst in kinds.items():
+        for gi in rng.permutation(len(lst))[:2]:
+            picks.append(lst[gi])
+    src_tok = np.empty(cfg.R * cfg.C, dtype=np.int64)
+    src_tok[dest.ravel()] = np.repeat(np.arange(cfg.R * cfg.S), cfg.K)
+    for (q, w, row0, rows, kind, idx) in picks:
+        e = w if w < cfg.E else next(en.e for en in plan.entries if en.q == q and en.w == w)
+        W13, W2 = _expert_np(layer.w13[e]), _expert_np(layer.w2[e])
+        sel = row0 + rng.choice(rows, size=min(rows, 8), replace=False)
+        X = O.layer._f64(xb.reshape(-1, cfg.H)[src_tok[sel]])
+        assert np.array_equal(bits_of(layer.recv[torch.as_tensor(sel, device=DEV)]),
+                              xb.reshape(-1, cfg.H)[src_tok[sel]])
+        g = X @ W13
+        a = O.silu(g[:, :cfg.I]) * g[:, cfg.I:]
+        yref = a @ W2
+        got = f64_of(layer.y[torch.as_tensor(sel, device=DEV)])
+        err = max_row_rel(got, yref)
+        say(f"  {kind} group q={q} w={w} e={e} rows={rows}: y max row rel {err:.3e}")
+        assert err <= TOL
+
+
+def test_full_layer_backward_experts():
+    """Training at maxvio 8 with B=4: full dW of a fallback expert, a slot-replicated expert
+    and a plain expert after reduce_grad, against the plan-free gradient."""
+    cfg = W.CONFIGS["train"].with_(maxvio=8.0)
+    topk, gates, xb, plan, dest, layer = _full_layer(cfg, cfg.B, True)
+    doutb = W.grad_rows(cfg.R, cfg.S, cfg.H, cfg.seed, "bf16")
+    layer.forward(bf16_from_bits(xb), i32(topk), f32(gates))
+    layer.backward(bf16_from_bits(doutb), f32(gates))
+    torch.cuda.synchronize()
+    fb = sorted({en.e for en in plan.entries if en.w < cfg.E})
+    sl = sorted({en.e for en in plan.entries if en.w >= cfg.E} - set(fb))
+    rep = {en.e for en in plan.entries}
+    plain = [e for e in range(cfg.E) if e not in rep and plan.L[e] > 0]
+    chosen = ([fb[0]] if fb else []) + [sl[0], min(plain, key=lambda e: plan.L[e])]
+    say("  experts", chosen, "fallback experts", fb)
+    for e in chosen:
+        W13 = layer.w13[e].cpu().view(torch.int16).numpy().view(np.uint16)
+        W2 = layer.w2[e].cpu().view(torch.int16).numpy().view(np.uint16)
+        # the plan-free gradient of expert e: every (token, k) routed to e, whatever rank serves it
+        r_i, s_i, k_i = np.nonzero(topk == e)
+        xe = O.layer._f64(xb[r_i, s_i])
+        g = xe @ O.layer._f64(W13)
+        gt, u = g[:, :cfg.I], g[:, cfg.I:]
+        a = O.silu(gt) * u
+        dy = np.asarray(gates, np.float64)[r_i, s_i, k_i][:, None] * O.layer._f64(doutb[r_i, s_i])
+        da = dy @ O.layer._f64(W2).T
+        sg = 1.0 / (1.0 + np.exp(-gt))
+        dgu = np.concatenate([da * u * sg * (1.0 + gt * (1.0 - sg)), da * O.silu(gt)], axis=1)
+        ref13 = xe.T @ dgu
+        ref2 = a.T @ dy
+        e13 = rel_fro(f64_of(layer.dw13[e]), ref13)
+        e2 = rel_fro(f64_of(layer.dw2[e]), ref2)
+        say(f"  expert {e} (L={plan.L[e]}): dW13 {e13:.3e} dW2 {e2:.3e}")
+        assert e13 <= TOL and e2 <= TOL
+    assert not layer.dw13_red.any() and not layer.dw2_red.any()

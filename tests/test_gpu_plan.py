@@ -1,0 +1,236 @@
+"""GPU parity of planning, dispatch and combine against the CPU oracle.
+
+Plan, cu_seqlens, dest, stats and permuted rows must be bit-exact; combine within
+1e-2 (max over tokens of the row-wise relative L2 error) of the float64 oracle.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import balanced_token_dispatch_moonep_amd as M
+import oracle as O
+import workload as W
+
+from gpu_util import (DEV, say, dims_of, i32, f32, bf16_from_bits, bits_of, f64_of, rows_tensor,
+                      run_plan, assert_plan_parity, max_row_rel)
+
+pytestmark = pytest.mark.gpu
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold():
+    with open(os.path.join(GOLD, "plan_worked.json")) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _gold(), ids=lambda c: c["name"])
+def test_plan_worked_examples(case):
+    say("plan worked example", case["name"])
+    topk = np.array(case["topk"], dtype=np.int32)
+    d = M.Dims.make(case["R"], case["E"], case["B"], case["S"], case["K"], 8)
+    plan, dest, (ws, cu, dd, st) = assert_plan_parity(d, topk)
+    assert dd.cpu().numpy().tolist() == case["dest"]
+    assert cu.cpu().numpy().tolist() == case["cu"]
+
+
+@pytest.mark.parametrize("lam", [0.0, 0.5, 1.0, 2.0])
+@pytest.mark.parametrize("B", [0, 2, 4])
+def test_plan_tiny_sweep(lam, B):
+    for seed in range(5):
+        cfg = W.CONFIGS["tiny"].with_(lam=lam, seed=seed)
+        topk, _, _ = W.routing_for(cfg)
+        say("plan tiny", lam, B, seed)
+        assert_plan_parity(dims_of(cfg, B=B, training=True), topk, training=True)
+
+
+@pytest.mark.parametrize("R,E,S,K,B,lam", [
+    (8, 64, 128, 4, 2, 0.5), (8, 64, 130, 4, 8, 1.5), (2, 16, 64, 8, 1, 1.0),
+    (1, 8, 32, 2, 0, 1.0), (8, 256, 64, 8, 4, 0.3), (4, 8, 65, 8, 2, 0.0), (16, 512, 96, 8, 3, 0.8),
+    (3, 12, 200, 3, 1, 1.2),
+])
+def test_plan_shapes(R, E, S, K, B, lam):
+    cfg = W.Config("m", R=R, E=E, B=B, S=S, K=K, H=8, I=0, dtype="f32", lam=lam, seed=3)
+    topk, _, _ = W.routing_for(cfg)
+    say("plan shape", R, E, S, K, B, lam)
+    assert_plan_parity(dims_of(cfg), topk)
+
+
+@pytest.mark.parametrize("maxvio", [0.0, 0.5, 2.0, 4.0, 8.0])
+def test_plan_full_size(maxvio):
+    cfg = W.CONFIGS["skew"].with_(maxvio=maxvio)
+    topk, _, _ = W.routing_for(cfg)
+    say("plan full size maxvio", maxvio)
+    for B in (4, 3):
+        plan, dest, (ws, cu, dd, st) = assert_plan_parity(dims_of(cfg, B=B), topk)
+        s = st.cpu().numpy()
+        assert s[13] == cfg.R * cfg.C and s[0] == 0
+
+
+def test_plan_is_deterministic():
+    cfg = W.CONFIGS["skew"].with_(maxvio=8.0)
+    topk, _, _ = W.routing_for(cfg)
+    d = dims_of(cfg)
+    tk = i32(topk)
+    first = [t.cpu().clone() for t in run_plan(d, topk, tk)[1:]]
+    for _ in range(3):
+        again = run_plan(d, topk, tk)[1:]
+        for a, b in zip(first, again):
+            assert torch.equal(a, b.cpu())
+
+
+def test_plan_invalid_routing_sets_status_and_no_rows():
+    cfg = W.CONFIGS["tiny"]
+    topk, _, _ = W.routing_for(cfg)
+    d = dims_of(cfg)
+    bad = topk.copy()
+    bad[1, 3, 0] = cfg.E          # out of range
+    _, cu, dest, st = run_plan(d, bad)
+    assert st.cpu().numpy()[0] & M.ST_BAD_ID
+    assert (dest.cpu().numpy() == -1).all()
+    assert (cu.cpu().numpy() == 0).all()
+    dup = topk.copy()
+    dup[2, 5, 1] = dup[2, 5, 0]   # duplicate expert in one token
+    _, cu, dest, st = run_plan(d, dup)
+    assert st.cpu().numpy()[0] & M.ST_DUP_ID
+    assert (dest.cpu().numpy() == -1).all()
+    # dispatch and combine skip rows whose dest is -1
+    x = torch.randn((cfg.R, cfg.S, cfg.H), device=DEV)
+    recv = torch.full((cfg.R * cfg.C, cfg.H), 3.0, device=DEV)
+    M.moonep_dispatch(d, dest, x, None, recv)
+    out = torch.full_like(x, 5.0)
+    M.moonep_combine(d, dest, recv, None, out)
+    torch.cuda.synchronize()
+    assert bool((recv == 3.0).all()) and bool((out == 0.0).all())
+
+
+def test_plan_training_fallback_flag():
+    cfg = W.CONFIGS["tiny"].with_(lam=2.0)
+    topk, _, _ = W.routing_for(cfg)
+    plan, _, (_, _, _, st) = assert_plan_parity(dims_of(cfg, B=0, training=True), topk, training=True)
+    assert plan.entries and (st.cpu().numpy()[0] & M.ST_TRAIN_FALLBACK)
+
+
+# ----------------------------------------------------------------------------
+# dispatch
+# ----------------------------------------------------------------------------
+
+def _layer_inputs(cfg, B=None):
+    topk, gates, _ = W.routing_for(cfg)
+    x = W.hidden_rows(cfg.R, cfg.S, cfg.H, cfg.seed, cfg.dtype)
+    d = dims_of(cfg, B=B)
+    plan, dest, (ws, cu, dd, st) = assert_plan_parity(d, topk)
+    return topk, gates, x, d, plan, dest, dd
+
+
+@pytest.mark.parametrize("name,over", [
+    ("tiny", {}), ("tiny", {"S": 100, "lam": 2.0}),
+    ("balanced", {"S": 256, "H": 512}), ("skew", {"S": 192, "H": 1032, "maxvio": 8.0}),
+])
+def test_dispatch_bitexact(name, over):
+    cfg = W.CONFIGS[name].with_(**over)
+    topk, gates, x, d, plan, dest, dd = _layer_inputs(cfg)
+    say("dispatch", name, over)
+    xt = rows_tensor(x)
+    canary = float("nan")
+    recv = torch.full((cfg.R * cfg.C, cfg.H), canary, dtype=xt.dtype, device=DEV)
+    M.moonep_dispatch(d, dd, xt, None, recv)
+    torch.cuda.synchronize()
+    ref = O.dispatch(dest, x)
+    got = recv.cpu().numpy() if cfg.dtype == "f32" else bits_of(recv)
+    assert got.tobytes() == ref.tobytes()          # every row written, bit for bit
+
+
+@pytest.mark.parametrize("maxvio", [0.0, 8.0])
+def test_dispatch_full_size(maxvio):
+    cfg = W.CONFIGS["skew"].with_(maxvio=maxvio)
+    topk, _, _ = W.routing_for(cfg)
+    d = dims_of(cfg)
+    plan = O.make_plan(topk, cfg.E, cfg.B)
+    dest = O.destinations(topk, plan)
+    say("dispatch full size maxvio", maxvio)
+    _, cu, dd, st = run_plan(d, topk)
+    np.testing.assert_array_equal(dd.cpu().numpy(), dest)
+    x = bf16_from_bits(W.hidden_rows(cfg.R, cfg.S, cfg.H, cfg.seed, "bf16"))
+    recv = torch.empty((cfg.R * cfg.C, cfg.H), dtype=torch.bfloat16, device=DEV)
+    recv.view(torch.int16).fill_(-1)
+    M.moonep_dispatch(d, dd, x, None, recv)
+    torch.cuda.synchronize()
+    # dest is a permutation (checked against the oracle above): each row must equal its token
+    src_tok = torch.empty(cfg.R * cfg.C, dtype=torch.long, device=DEV)
+    src_tok[dd.view(-1).long()] = torch.arange(cfg.R * cfg.S, device=DEV).repeat_interleave(cfg.K)
+    xs = x.view(-1, cfg.H)
+    for lo in range(0, cfg.R * cfg.C, 32768):
+        hi = lo + 32768
+        assert torch.equal(recv[lo:hi].view(torch.int16), xs[src_tok[lo:hi]].view(torch.int16))
+
+
+def test_dispatch_row_scale():
+    cfg = W.CONFIGS["skew"].with_(S=128, H=512, maxvio=4.0)
+    topk, gates, x, d, plan, dest, dd = _layer_inputs(cfg)
+    dout = W.grad_rows(cfg.R, cfg.S, cfg.H, 1, "bf16")
+    recv = torch.empty((cfg.R * cfg.C, cfg.H), dtype=torch.bfloat16, device=DEV)
+    M.moonep_dispatch(d, dd, bf16_from_bits(dout), f32(gates), recv)
+    torch.cuda.synchronize()
+    ref = O.dispatch(dest, dout, row_scale=gates)
+    got = f64_of(recv)
+    # one float32 product rounded once to bf16: within half a bf16 ulp (2^-9 relative)
+    assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-30)
+
+
+# ----------------------------------------------------------------------------
+# combine
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,over,gated", [
+    ("tiny", {}, True), ("tiny", {"S": 100, "lam": 2.0}, False),
+    ("skew", {"S": 192, "H": 1032, "maxvio": 8.0}, True), ("balanced", {"S": 128, "H": 512, "K": 3}, True),
+    ("balanced", {"S": 64, "H": 256, "K": 5}, False),
+])
+def test_combine_vs_oracle(name, over, gated):
+    cfg = W.CONFIGS[name].with_(**over)
+    topk, gates, x, d, plan, dest, dd = _layer_inputs(cfg)
+    say("combine", name, over, gated)
+    rng = np.random.default_rng(11)
+    yv = rng.standard_normal((cfg.R * cfg.C, cfg.H)).astype(np.float32)
+    y = yv if cfg.dtype == "f32" else W.bf16_bits(yv)
+    out = torch.empty((cfg.R, cfg.S, cfg.H), dtype=torch.float32 if cfg.dtype == "f32" else torch.bfloat16,
+                      device=DEV)
+    M.moonep_combine(d, dd, rows_tensor(y), f32(gates) if gated else None, out)
+    torch.cuda.synchronize()
+    ref = O.combine(dest, y, gates if gated else None)
+    err = max_row_rel(f64_of(out), ref)
+    say("  max row rel err", err)
+    assert err <= 1e-2
+
+
+@pytest.mark.parametrize("maxvio", [0.0, 4.0])
+def test_round_trip_full_size(maxvio):
+    """Identity experts: combine(dispatch(x)) with gates summing to 1 returns x (bf16 rounding)."""
+    cfg = W.CONFIGS["skew"].with_(maxvio=maxvio)
+    topk, gates, _ = W.routing_for(cfg)
+    d = dims_of(cfg)
+    say("round trip full size", maxvio)
+    _, cu, dd, st = run_plan(d, topk)
+    xb = W.hidden_rows(cfg.R, cfg.S, cfg.H, cfg.seed, "bf16")
+    x = bf16_from_bits(xb)
+    recv = torch.empty((cfg.R * cfg.C, cfg.H), dtype=torch.bfloat16, device=DEV)
+    out = torch.empty_like(x)
+    M.moonep_dispatch(d, dd, x, None, recv)
+    g = f32(gates)
+    M.moonep_combine(d, dd, recv, g, out)
+    torch.cuda.synchronize()
+    num = (out.float() - x.float()).norm(dim=-1)
+    den = x.float().norm(dim=-1)
+    assert float((num / den).max()) <= 1e-2
+    # sampled tokens against the oracle's combine
+    plan = O.make_plan(topk, cfg.E, cfg.B)
+    dest = O.destinations(topk, plan)
+    np.testing.assert_array_equal(dd.cpu().numpy(), dest)
+    rng = np.random.default_rng(5)
+    for (r, s) in zip(rng.integers(0, cfg.R, 64), rng.integers(0, cfg.S, 64)):
+        ref = sum(float(gates[r, s, k]) * W.bf16_to_f32(xb[r, s]).astype(np.float64) for k in range(cfg.K))
+        got = f64_of(out[r, s])
+        assert np.linalg.norm(got - ref) <= 1e-2 * np.linalg.norm(ref)
