@@ -16,6 +16,7 @@ constexpr int kMaxE = 1024;
 constexpr int kMaxG = 64;            // home experts per rank
 constexpr int kMaxB = 64;
 constexpr int kMaxK = 16;
+constexpr int kZeroElems = 512;      // zero bf16 elements kept in the plan workspace
 
 // Header words of the plan workspace.
 enum HdrWord {
@@ -63,6 +64,7 @@ struct PlanWs {
     Segment* fb_seg;       // [E][kMaxR]
     Segment* home_seg;     // [E]
     int32_t* counters;     // [64] scratch counters for persistent kernels
+    uint16_t* zeros;       // [kZeroElems] zero bf16 row segment (source of masked GEMM tile loads)
 };
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -101,6 +103,7 @@ inline size_t plan_ws_layout(const moonep_dims_t* d, void* base, PlanWs* ws) {
     w.fb_seg = (Segment*)take(E * kMaxR * sizeof(Segment));
     w.home_seg = (Segment*)take(E * sizeof(Segment));
     w.counters = (int32_t*)take(64 * 4);
+    w.zeros = (uint16_t*)take(kZeroElems * 2);
     (void)R;
     if (ws) *ws = w;
     return off;

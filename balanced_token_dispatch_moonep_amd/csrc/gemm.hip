@@ -12,46 +12,55 @@
 //
 // Kernel design (MI355X / CDNA4):
 //   * 256x256 output tile per workgroup, 4 waves in 2x2, each wave 128x128 = 4x4 tiles
-//     of v_mfma_f32_32x32x16_bf16 (bf16 inputs, fp32 accumulation).  K step 64.
-//   * Operands staged through LDS in a k-contiguous layout with a 16-byte row pad
-//     (conflict-free 128-bit fragment reads), double-buffered: global loads of step
-//     k+1 are in flight while the MFMAs of step k run; one barrier per step.
-//   * Operands stored k-contiguous in HBM are copied as 16-byte rows; operands stored
-//     m/n-contiguous (weights in the forward, both operands of dW) are loaded as 8x8
-//     bf16 blocks and transposed in registers with v_perm_b32 before the LDS store.
+//     of v_mfma_f32_32x32x16_bf16 (bf16 inputs, fp32 accumulation).  K step 32.
+//   * Operand tiles go HBM -> LDS with global_load_lds_dwordx4 (16 bytes per lane, no
+//     register staging), through a 4-stage ring: loads run three K steps ahead of the
+//     matrix cores; one explicit vmcnt wait and one barrier per step.
+//   * LDS tiles are XOR-swizzled in 16-byte chunks so fragment reads are bank-conflict
+//     free.  k-contiguous operands (activations, backward weights) are read with
+//     ds_read_b128; m/n-contiguous operands (forward weights, both dW operands) stay
+//     m/n-contiguous in LDS and are read with ds_read_b64_tr_b16, which hands each lane
+//     4 consecutive k of one column -- two of them make one MFMA fragment.
 //   * Persistent grid (one workgroup per CU).  Tiles are ordered group-major, then
 //     n-tile, then m-tile, and each XCD (blockIdx % 8) takes a contiguous range of them,
-//     so the tiles that share a weight panel or an activation panel run on the same XCD
-//     at the same time and hit its L2.
-//   * Epilogues are fused: SwiGLU (act = silu(gate) * up, with Gt|U saved) after the
-//     gate/up GEMM; SwiGLU' (dGt, dU written over the saved Gt|U) after dA = dY W2^T;
-//     fp32 accumulate into the home or reduce-buffer gradient for dW.
+//     so tiles sharing a weight or activation panel run on the same XCD together.
+//   * Masked rows/columns of a tile load from a zero row kept in the plan workspace.
+//   * Epilogues are fused and staged through LDS for 16-byte stores: SwiGLU (act =
+//     silu(gate) * up, Gt|U saved) after the gate/up GEMM; SwiGLU' (dGt, dU written over
+//     the saved Gt|U) after dA = dY W2^T; fp32 accumulate into the home or reduce-buffer
+//     gradient for dW.
 #include "common.h"
 
 namespace moonep {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int LDK = BK + 8;                  // LDS row pitch (bf16 elements): 144 bytes
-constexpr int TILE_ELEMS = BM * LDK;         // one operand, one stage
-constexpr int GEMM_SMEM = 4 * TILE_ELEMS * 2;  // 2 stages x (A, B), bytes = 147456
+constexpr int BM = 256, BN = 256, BK = 32, NSTAGE = 4;
+constexpr int OP_BYTES = 256 * BK * 2;             // one operand tile of one stage: 16 KiB
+constexpr int STAGE_BYTES = 2 * OP_BYTES;
+constexpr int GEMM_SMEM = NSTAGE * STAGE_BYTES;    // 128 KiB
+constexpr int EPL = 132;                           // fp32 pitch of a staged epilogue row
 constexpr int MAX_GROUPS = 2 * kMaxE;
+static_assert(4 * 32 * EPL * 4 <= GEMM_SMEM, "epilogue staging must fit in the stage ring");
 
 enum Epi { EPI_SWIGLU_FWD = 0, EPI_STORE = 1, EPI_SWIGLU_BWD = 2, EPI_ACC_F32 = 3 };
-enum BMode { B_NCONTIG = 0, B_KCONTIG = 1 };
+enum Mode { ROWS_BN = 0, ROWS_BK = 1 };   // weights n-contiguous ([K, N]) or k-contiguous ([N, K])
 
 struct GemmArgs {
     PlanWs w;
-    const uint16_t* A;        // rows modes: activations [R*C, lda]; dW: [R*C, lda] read transposed
+    const uint16_t* A;        // rows modes: activations [R*C, lda]; dW: [R*C, lda] (m-contiguous)
     int lda;
-    const uint16_t* B;        // dW: [R*C, ldb] read transposed
+    const uint16_t* B;        // dW: [R*C, ldb] (n-contiguous)
     const uint16_t* Bhome;    // rows modes: weights, home rows [E, ...]
     const uint16_t* Bslot;    //             slot rows [R*B, ...]
     long long bstride;        // elements per weight row
     int ldb;
-    int M, N, K;              // dW: output M x N; rows modes: N output cols, K reduction
+    int M, N, K;              // dW: output M x N; rows modes: N output columns, K reduction
     int I;                    // SwiGLU split
     uint16_t* out;            // EPI_STORE / EPI_SWIGLU_FWD (act): bf16 [R*C, ldo]
     int ldo;
@@ -61,54 +70,75 @@ struct GemmArgs {
     int ntiles_n;
 };
 
-__device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
+// ---------------------------------------------------------------------------
+// synchronisation and LDS tile layout
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+// Workgroup barrier without the memory fence of __syncthreads (which would wait for every
+// in-flight LDS DMA); LDS DMA completion is waited for explicitly with wait_vm.
+__device__ __forceinline__ void block_sync() {
+    compiler_fence();
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+}
+__device__ __forceinline__ void wave_sync() {
+    compiler_fence();
+    __builtin_amdgcn_wave_barrier();
+    compiler_fence();
+}
+// wait until at most N vector-memory operations of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
 
-// k-contiguous operand: tile row r (0..255) at src + r*ld, columns k0..k0+63 already in src.
-__device__ __forceinline__ void load_kc(uint4 (&v)[8], const uint16_t* src, int ld, int nvalid, int tid) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int c = i * 256 + tid;
-        const int r = c >> 3, kc = c & 7;
-        v[i] = r < nvalid ? *reinterpret_cast<const uint4*>(src + (size_t)r * ld + kc * 8) : zero4();
-    }
-}
-__device__ __forceinline__ void store_kc(const uint4 (&v)[8], uint16_t* lds, int tid) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int c = i * 256 + tid;
-        const int r = c >> 3, kc = c & 7;
-        *reinterpret_cast<uint4*>(lds + r * LDK + kc * 8) = v[i];
-    }
+// wait until every LDS access of this wave has completed
+__device__ __forceinline__ void wait_lgkm0() {
+    __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));
 }
 
-// m/n-contiguous operand: this thread's 8x8 block = k rows kb*8..+7 (src points at row kb*8,
-// column of the block), kvalid rows of the step are real.
-__device__ __forceinline__ void load_t(uint4 (&v)[8], const uint16_t* src, int ld, int kvalid, bool ok) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        v[i] = (ok && i < kvalid) ? *reinterpret_cast<const uint4*>(src + (size_t)i * ld) : zero4();
+// k-contiguous tile [256 rows][32 k]: 16-byte chunk (r, c), c = k/8 in 0..3
+__device__ __forceinline__ int kc_pos(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
+// m/n-contiguous tile [32 k][256 mn]: 16-byte chunk (k, c), c = mn/8 in 0..31
+__device__ __forceinline__ int mn_pos(int k, int c) { return k * 32 + (c ^ ((k & 3) << 2)); }
+
+// HBM -> LDS copy of 16 bytes per lane: lane l's bytes land at lds + 16*l (lds is wave-uniform).
+// Issued as inline asm so the compiler does not track it as an LDS write (it would otherwise
+// drain every in-flight copy before each transposing LDS read); completion is awaited with
+// wait_vm() and a barrier before the data is read.  The instruction has no register outputs.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"   // m0 is reserved: nothing else in these kernels uses it
+// HBM -> LDS copy of 16 bytes per lane: lane l's bytes land at LDS byte address lds + 16*l (lds is
+// wave-uniform).  Issued as inline asm so the compiler does not track it as an LDS write (it would
+// otherwise drain every in-flight copy before each transposing LDS read); completion is awaited
+// with wait_vm() and a barrier before the data is read.  The instruction has no register outputs.
+__device__ __forceinline__ void dma16(const uint16_t* g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
+                 : "memory", "m0");
 }
-// transpose the 8x8 bf16 block in registers and store 8 k-contiguous 16-byte rows
-__device__ __forceinline__ void store_t(const uint4 (&v)[8], uint16_t* lds, int tid) {
-    const int kb = tid >> 5, mb = tid & 31;
-    uint32_t in[8][4];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        in[i][0] = v[i].x;
-        in[i][1] = v[i].y;
-        in[i][2] = v[i].z;
-        in[i][3] = v[i].w;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-        uint4 o;
-        o.x = __builtin_amdgcn_perm(in[1][j >> 1], in[0][j >> 1], sel);
-        o.y = __builtin_amdgcn_perm(in[3][j >> 1], in[2][j >> 1], sel);
-        o.z = __builtin_amdgcn_perm(in[5][j >> 1], in[4][j >> 1], sel);
-        o.w = __builtin_amdgcn_perm(in[7][j >> 1], in[6][j >> 1], sel);
-        *reinterpret_cast<uint4*>(lds + (mb * 8 + j) * LDK + kb * 8) = o;
-    }
+#pragma clang diagnostic pop
+// LDS byte address of a pointer into dynamic shared memory
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)reinterpret_cast<uintptr_t>((lds_void_t*)(p));
+}
+
+// MFMA fragment (32 rows/cols x 16 k) from a k-contiguous tile: one 16-byte read per lane
+__device__ __forceinline__ bf16x8_t frag_kc(const char* T, int rb, int kk, int lane) {
+    const int r = rb + (lane & 31), c = kk * 2 + (lane >> 5);
+    return *reinterpret_cast<const bf16x8_t*>(T + kc_pos(r, c) * 16);
+}
+// same fragment from an m/n-contiguous tile: lane l gets column mb + l%32, k = 8*(l/32) + 0..7,
+// as two transposing reads of 4 k each (lanes of a 16-lane group address a 4 k x 16 col block)
+__device__ __forceinline__ bf16x8_t frag_mn(const char* T, int mb, int kk, int lane) {
+    const int G = lane >> 4, i = lane & 15;
+    const int col = mb + 16 * (G & 1) + 4 * (i & 3);
+    const int k = kk * 16 + 8 * (G >> 1) + (i >> 2);
+    const char* p = T + mn_pos(k, col >> 3) * 16 + (col & 7) * 2;
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p + 4 * 32 * 16));
+    const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8_t, v);
 }
 
 // LDS column (tile n index) of wave-local MFMA column tile tj.
@@ -118,26 +148,34 @@ __device__ __forceinline__ int bcol(int wn, int tj) {
     return wn * 128 + tj * 32;
 }
 
-template <int EPI>
-__device__ __forceinline__ void mma_step(f32x16_t (&acc)[4][4], const uint16_t* As, const uint16_t* Bs,
-                                         int wm, int wn, int lane) {
-    const int lr = lane & 31, lk = (lane >> 5) * 8;
+// MFMA operand fragments of one 16-k slice of a stage: 4 row tiles of A, 4 column tiles of B.
+struct Frags {
+    bf16x8_t a[4], b[4];
+};
+
+template <bool A_KC, bool B_KC, int EPI>
+__device__ __forceinline__ void load_frags(Frags& f, const char* st, int kk, int wm, int wn, int lane) {
+    const char* As = st;
+    const char* Bs = st + OP_BYTES;
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-        bf16x8_t af[4], bfr[4];
+    for (int t = 0; t < 4; ++t)
+        f.a[t] = A_KC ? frag_kc(As, wm * 128 + t * 32, kk, lane) : frag_mn(As, wm * 128 + t * 32, kk, lane);
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-            af[t] = *reinterpret_cast<const bf16x8_t*>(As + (wm * 128 + t * 32 + lr) * LDK + kk * 16 + lk);
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-            bfr[t] = *reinterpret_cast<const bf16x8_t*>(Bs + (bcol<EPI>(wn, t) + lr) * LDK + kk * 16 + lk);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
+    for (int t = 0; t < 4; ++t)
+        f.b[t] = B_KC ? frag_kc(Bs, bcol<EPI>(wn, t), kk, lane) : frag_mn(Bs, bcol<EPI>(wn, t), kk, lane);
 }
+
+__device__ __forceinline__ void mma_row(f32x16_t (&acc)[4][4], const Frags& f, int i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+}
+__device__ __forceinline__ void mma_frags(f32x16_t (&acc)[4][4], const Frags& f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mma_row(acc, f, i);
+}
+
+__device__ __forceinline__ float sigm(float x) { return 1.0f / (1.0f + __expf(-x)); }
 
 // Rows of a plan group, or 0 if the descriptor is out of range (never for a valid plan).
 __device__ __forceinline__ int group_rows(const Group& g, const PlanWs& w) {
@@ -150,28 +188,76 @@ __device__ __forceinline__ bool seg_ok(const Segment& s, const PlanWs& w) {
     return s.row0 >= 0 && s.rows >= 0 && (long long)s.row0 + s.rows <= (long long)w.R * w.C;
 }
 
-__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
-__device__ __forceinline__ uint16_t f2bf16(float f) { return (uint16_t)f2bf(f); }
-__device__ __forceinline__ float sigm(float x) { return 1.0f / (1.0f + __expf(-x)); }
-
-// ---------------------------------------------------------------------------
-// Epilogues.  The tile's accumulators are staged through LDS (each wave owns a
-// 64 x 128 fp32 region, two halves per tile), then every lane handles 8 (or 4)
-// consecutive columns so global stores are 16 bytes wide and row-contiguous.
-// C layout of a 32x32 MFMA tile: lane l, reg r -> row (r/4)*8 + (l/32)*4 + r%4, col l%32.
-// ---------------------------------------------------------------------------
-constexpr int EPL = 132;   // fp32 pitch of a staged row (128 + 4 pad)
-
-template <int h>
-__device__ __forceinline__ void stage_half(const f32x16_t (&acc)[4][4], float* ep, int lane) {
-    const int lc = lane & 31, lr4 = (lane >> 5) * 4;
+__device__ __forceinline__ void zero_acc(f32x16_t (&acc)[4][4]) {
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                ep[(ii * 32 + (r >> 2) * 8 + lr4 + (r & 3)) * EPL + j * 32 + lc] = acc[2 * h + ii][j][r];
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+}
+
+// Main loop over nst K-steps of 32 (two 16-k slices each).  issue(s, buf, part) enqueues
+// this wave's DMA loads of step s (part p = one load per operand, p = 0..3) into a ring of
+// NSTAGE buffers.  Fragments are double-buffered in registers: the reads of the next slice are
+// issued before the MFMAs of the current one; the step barrier sits between a step's two slices
+// so the MFMAs already issued keep the matrix cores busy across it; and the DMA loads of step
+// s+3 are spread between the MFMAs of the second slice, so no burst of memory instructions
+// stalls the wave's in-order issue while the matrix pipe drains.
+template <bool A_KC, bool B_KC, int EPI, typename Issue>
+__device__ __forceinline__ void pipeline(f32x16_t (&acc)[4][4], char* smem, int nst, int wm, int wn, int lane,
+                                         Issue&& issue) {
+    wait_vm<0>();     // previous tile's epilogue stores are older than this tile's DMA
+#pragma unroll
+    for (int s = 0; s < NSTAGE - 1; ++s)
+        if (s < nst)
+#pragma unroll
+            for (int p = 0; p < 4; ++p) issue(s, s, p);
+    if (nst >= 3) wait_vm<16>();
+    else if (nst == 2) wait_vm<8>();
+    else wait_vm<0>();
+    block_sync();
+    Frags f0, f1;
+    load_frags<A_KC, B_KC, EPI>(f0, smem, 0, wm, wn, lane);
+    for (int s = 0; s < nst; ++s) {
+        const char* st = smem + (s & (NSTAGE - 1)) * STAGE_BYTES;
+        load_frags<A_KC, B_KC, EPI>(f1, st, 1, wm, wn, lane);
+        mma_frags(acc, f0);
+        // slice-1 fragments were read long ago; settling them here keeps the compiler from making
+        // the next MFMAs wait on the reads issued after the barrier
+        wait_lgkm0();
+        if (s + 1 < nst) {
+            // step s+1 must have landed: only step s+2 may still be in flight
+            if (s + 2 < nst) wait_vm<8>();
+            else wait_vm<0>();
+            block_sync();
+            load_frags<A_KC, B_KC, EPI>(f0, smem + ((s + 1) & (NSTAGE - 1)) * STAGE_BYTES, 0, wm, wn, lane);
+        }
+        // every wave is past step s-1, so its buffer takes step s+3
+        const bool more = s + NSTAGE - 1 < nst;
+        const int nb = (s + NSTAGE - 1) & (NSTAGE - 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            mma_row(acc, f1, i);
+            if (more) issue(s + NSTAGE - 1, nb, i);
+        }
+    }
+    block_sync();     // every wave is done with the ring before the epilogue reuses it
+}
+
+// ---------------------------------------------------------------------------
+// Epilogues: each wave stages a 32 x 128 fp32 quarter of its accumulators in its own LDS
+// region, then every lane handles 8 (or 4) consecutive columns of a row so global accesses
+// are 16 bytes wide.  C layout of a 32x32 MFMA tile: lane l, reg r -> row (r/4)*8 + (l/32)*4
+// + r%4, column l%32.
+// ---------------------------------------------------------------------------
+template <int q>
+__device__ __forceinline__ void stage_quarter(const f32x16_t (&acc)[4][4], float* ep, int lane) {
+    const int lc = lane & 31, lr4 = (lane >> 5) * 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ep[((r >> 2) * 8 + lr4 + (r & 3)) * EPL + j * 32 + lc] = acc[q][j][r];
 }
 
 __device__ __forceinline__ uint4 pack8(const float (&v)[8]) {
@@ -187,22 +273,21 @@ __device__ __forceinline__ void read8(const float* p, float (&v)[8]) {
     v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w; v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
 }
 
-template <int EPI, int h>
-__device__ __forceinline__ void epilogue_rows_half(const GemmArgs& a, const f32x16_t (&acc)[4][4], uint16_t* smem,
-                                                   int wm, int wn, int lane, int nt, int row0, int mvalid) {
-    float* ep = reinterpret_cast<float*>(smem) + (wm * 2 + wn) * 64 * EPL;
-    {
-        stage_half<h>(acc, ep, lane);
-        __syncthreads();
-        const int rbase = wm * 128 + h * 64;   // tile-local row of the region's first row
-        if (EPI == EPI_SWIGLU_FWD) {
-            // region columns 0..63 = gate, 64..127 = up, for act columns nt*128 + wn*64 + c
-            const int I = a.I;
-            const int c = (lane & 7) * 8;
-            const int col = nt * 128 + wn * 64 + c;
-            for (int it = 0; it < 8; ++it) {
-                const int rr = it * 8 + (lane >> 3);
-                if (rbase + rr >= mvalid || col >= I) continue;
+template <int EPI, int q>
+__device__ __forceinline__ void epi_rows_quarter(const GemmArgs& a, const f32x16_t (&acc)[4][4], float* ep, int wm,
+                                                 int wn, int lane, int nt, int row0, int mvalid) {
+    stage_quarter<q>(acc, ep, lane);
+    wave_sync();
+    const int rbase = wm * 128 + q * 32;   // tile-local row of the quarter's first row
+    if (EPI == EPI_SWIGLU_FWD) {
+        // staged columns 0..63 = gate, 64..127 = up, for act columns nt*128 + wn*64 + c
+        const int I = a.I;
+        const int c = (lane & 7) * 8;
+        const int col = nt * 128 + wn * 64 + c;
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int rr = it * 8 + (lane >> 3);
+            if (rbase + rr < mvalid && col < I) {
                 float g[8], u[8], o[8];
                 read8(ep + rr * EPL + c, g);
                 read8(ep + rr * EPL + 64 + c, u);
@@ -215,89 +300,98 @@ __device__ __forceinline__ void epilogue_rows_half(const GemmArgs& a, const f32x
                     *reinterpret_cast<uint4*>(a.gu + row * 2 * I + I + col) = pack8(u);
                 }
             }
-        } else if (EPI == EPI_SWIGLU_BWD) {
-            const int I = a.I;
-            const int c = (lane & 15) * 8;
-            const int col = nt * BN + wn * 128 + c;
-            for (int it = 0; it < 16; ++it) {
-                const int rr = it * 4 + (lane >> 4);
-                if (rbase + rr >= mvalid || col >= I) continue;
+        }
+    } else if (EPI == EPI_SWIGLU_BWD) {
+        const int I = a.I;
+        const int c = (lane & 15) * 8;
+        const int col = nt * BN + wn * 128 + c;
+        // all loads first (clamped to in-bounds addresses), then compute and masked stores
+        uint4 gv[8], uv[8];
+        const int lcol = min(col, I - 8);
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            const int rr = it * 4 + (lane >> 4);
+            const size_t row = (size_t)(row0 + min(rbase + rr, mvalid - 1));
+            gv[it] = *reinterpret_cast<const uint4*>(a.gu + row * 2 * I + lcol);
+            uv[it] = *reinterpret_cast<const uint4*>(a.gu + row * 2 * I + I + lcol);
+        }
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            const int rr = it * 4 + (lane >> 4);
+            if (rbase + rr < mvalid && col < I) {
                 const size_t row = (size_t)(row0 + rbase + rr);
-                uint4* pg = reinterpret_cast<uint4*>(a.gu + row * 2 * I + col);
-                uint4* pu = reinterpret_cast<uint4*>(a.gu + row * 2 * I + I + col);
                 float da[8], g[8], u[8], dg[8], du[8];
                 read8(ep + rr * EPL + c, da);
-                unpack8(*pg, g);
-                unpack8(*pu, u);
+                unpack8(gv[it], g);
+                unpack8(uv[it], u);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const float sg = sigm(g[i]);
                     dg[i] = da[i] * u[i] * sg * (1.0f + g[i] * (1.0f - sg));
                     du[i] = da[i] * g[i] * sg;
                 }
-                *pg = pack8(dg);
-                *pu = pack8(du);
+                *reinterpret_cast<uint4*>(a.gu + row * 2 * I + col) = pack8(dg);
+                *reinterpret_cast<uint4*>(a.gu + row * 2 * I + I + col) = pack8(du);
             }
-        } else {
-            const int c = (lane & 15) * 8;
-            const int col = nt * BN + wn * 128 + c;
-            for (int it = 0; it < 16; ++it) {
-                const int rr = it * 4 + (lane >> 4);
-                if (rbase + rr >= mvalid || col >= a.N) continue;
+        }
+    } else {
+        const int c = (lane & 15) * 8;
+        const int col = nt * BN + wn * 128 + c;
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            const int rr = it * 4 + (lane >> 4);
+            if (rbase + rr < mvalid && col < a.N) {
                 float v[8];
                 read8(ep + rr * EPL + c, v);
                 *reinterpret_cast<uint4*>(a.out + (size_t)(row0 + rbase + rr) * a.ldo + col) = pack8(v);
             }
         }
-        __syncthreads();
     }
+    wave_sync();
 }
 
-template <int EPI>
-__device__ __forceinline__ void epilogue_rows(const GemmArgs& a, const f32x16_t (&acc)[4][4], uint16_t* smem,
-                                              int wm, int wn, int lane, int nt, int row0, int mvalid) {
-    epilogue_rows_half<EPI, 0>(a, acc, smem, wm, wn, lane, nt, row0, mvalid);
-    epilogue_rows_half<EPI, 1>(a, acc, smem, wm, wn, lane, nt, row0, mvalid);
-}
-
-template <int h>
-__device__ __forceinline__ void epilogue_dw_half(const GemmArgs& a, const f32x16_t (&acc)[4][4], uint16_t* smem,
-                                            int wm, int wn, int lane, float* out, int m0, int n0) {
-    float* ep = reinterpret_cast<float*>(smem) + (wm * 2 + wn) * 64 * EPL;
-    {
-        stage_half<h>(acc, ep, lane);
-        __syncthreads();
-        const int c = (lane & 31) * 4;
-        const int col = n0 + wn * 128 + c;
-        for (int it = 0; it < 32; ++it) {
-            const int rr = it * 2 + (lane >> 5);
-            const int row = m0 + wm * 128 + h * 64 + rr;
-            if (row >= a.M || col >= a.N) continue;
-            const float4 v = *reinterpret_cast<const float4*>(ep + rr * EPL + c);
-            float4* p = reinterpret_cast<float4*>(out + (size_t)row * a.N + col);
-            float4 o = *p;
-            o.x += v.x;
-            o.y += v.y;
-            o.z += v.z;
-            o.w += v.w;
-            *p = o;
+template <int q>
+__device__ __forceinline__ void epi_dw_quarter(const GemmArgs& a, const f32x16_t (&acc)[4][4], float* ep, int wm,
+                                               int wn, int lane, float* out, int m0, int n0) {
+    stage_quarter<q>(acc, ep, lane);
+    wave_sync();
+    const int c = (lane & 31) * 4;
+    const int col = n0 + wn * 128 + c;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        // all loads first (clamped to in-bounds addresses), then add and masked stores
+        float4 old[8];
+        const int lcol = min(col, a.N - 4);
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            const int rr = (half * 8 + it) * 2 + (lane >> 5);
+            const int row = min(m0 + wm * 128 + q * 32 + rr, a.M - 1);
+            old[it] = *reinterpret_cast<const float4*>(out + (size_t)row * a.N + lcol);
         }
-        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            const int rr = (half * 8 + it) * 2 + (lane >> 5);
+            const int row = m0 + wm * 128 + q * 32 + rr;
+            if (row < a.M && col < a.N) {
+                const float4 v = *reinterpret_cast<const float4*>(ep + rr * EPL + c);
+                float4 o = old[it];
+                o.x += v.x;
+                o.y += v.y;
+                o.z += v.z;
+                o.w += v.w;
+                *reinterpret_cast<float4*>(out + (size_t)row * a.N + col) = o;
+            }
+        }
     }
-}
-
-__device__ __forceinline__ void epilogue_dw(const GemmArgs& a, const f32x16_t (&acc)[4][4], uint16_t* smem,
-                                            int wm, int wn, int lane, float* out, int m0, int n0) {
-    epilogue_dw_half<0>(a, acc, smem, wm, wn, lane, out, m0, n0);
-    epilogue_dw_half<1>(a, acc, smem, wm, wn, lane, out, m0, n0);
+    wave_sync();
 }
 
 // ---------------------------------------------------------------------------
-// Row-grouped GEMM: C[rows, N] = A[rows, K] * B_w[K, N] per plan group.
+// Row-grouped GEMM: C[rows, N] = A[rows, K] * B_w[K, N] for every plan group.
 // ---------------------------------------------------------------------------
-template <int EPI, int BMODE>
+template <int MODE, int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_rows_kernel(GemmArgs a) {
-    extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
     __shared__ int s_pref[MAX_GROUPS + 1];
     __shared__ int s_part[256];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -327,9 +421,7 @@ __global__ __launch_bounds__(256, 1) void gemm_rows_kernel(GemmArgs a) {
             s_pref[g] = run;
             run += (group_rows(groups[g], a.w) + BM - 1) / BM;
         }
-        if (tid == 255) s_pref[ng] = run;   // lo + per covers ng for the last thread
-        __syncthreads();
-        if (tid == 0 && ng == 0) s_pref[0] = 0;
+        if (tid == 255) s_pref[ng] = run;
         __syncthreads();
     }
     const int NT = a.ntiles_n;
@@ -338,14 +430,11 @@ __global__ __launch_bounds__(256, 1) void gemm_rows_kernel(GemmArgs a) {
     const int xcd = blockIdx.x % nxcd, li = blockIdx.x / nxcd, per_wg = gridDim.x / nxcd;
     const int chunk = (total + nxcd - 1) / nxcd;
     const int t_lo = xcd * chunk, t_hi = min(total, t_lo + chunk);
-
-    uint16_t* As0 = smem;
-    uint16_t* Bs0 = smem + TILE_ELEMS;
-    uint16_t* As1 = smem + 2 * TILE_ELEMS;
-    uint16_t* Bs1 = smem + 3 * TILE_ELEMS;
+    float* ep = reinterpret_cast<float*>(smem) + wave * 32 * EPL;
+    const int nst = a.K / BK;
+    const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds_addr(smem) + wave * 4 * 1024);
 
     for (int t = t_lo + li; t < t_hi; t += per_wg) {
-        // decode tile -> group, n-tile, m-tile (binary search over the prefix)
         int lo = 0, hi = ng - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
@@ -360,78 +449,63 @@ __global__ __launch_bounds__(256, 1) void gemm_rows_kernel(GemmArgs a) {
         const int mvalid = min(BM, group_rows(gr, a.w) - mt * BM);
         const uint16_t* W = gr.wsel >= 0 ? a.Bhome + (size_t)gr.wsel * a.bstride
                                          : a.Bslot + (size_t)(-1 - gr.wsel) * a.bstride;
-        const uint16_t* Arow = a.A + (size_t)row0 * a.lda;
 
-        // per-thread B addressing
-        const uint16_t* Bsrc;
-        bool bok = true;
-        int bvalid = BN;
-        if (BMODE == B_NCONTIG) {
-            const int c = (tid & 31) * 8;      // tile column of this thread's 8x8 block
-            int gcol;
-            if (EPI == EPI_SWIGLU_FWD) {
-                const int cc = nt * 128 + (c & 127);
-                bok = cc < a.I;
-                gcol = c < 128 ? cc : a.I + cc;
-            } else {
-                gcol = nt * BN + c;
-                bok = gcol < a.N;
+        // per-lane sources of the 4 DMA loads per operand and step
+        const uint16_t* ap[4];
+        const uint16_t* bp[4];
+        bool bmove[4];
+        long long bstep;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int p = (wave * 4 + i) * 64 + lane;
+            {   // A: k-contiguous activations, rows beyond the group clamp to its last row
+                const int r = p >> 2, c = (p & 3) ^ ((r >> 2) & 3);
+                ap[i] = a.A + (size_t)(row0 + min(r, mvalid - 1)) * a.lda + c * 8;
             }
-            Bsrc = W + (size_t)((tid >> 5) * 8) * a.ldb + (bok ? gcol : 0);
-        } else {
-            Bsrc = W + (size_t)(nt * BN) * a.ldb;
-            bvalid = min(BN, a.N - nt * BN);
+            if (MODE == ROWS_BK) {   // weights [N, K]
+                const int r = p >> 2, c = (p & 3) ^ ((r >> 2) & 3);
+                const int n = nt * BN + r;
+                bmove[i] = n < a.N;
+                bp[i] = bmove[i] ? W + (size_t)n * a.ldb + c * 8 : a.w.zeros + c * 8;
+            } else {                 // weights [K, N]
+                const int k = p >> 5, c = (p & 31) ^ ((k & 3) << 2);
+                int col;
+                if (EPI == EPI_SWIGLU_FWD) {
+                    const int cc = nt * 128 + (c & 15) * 8;
+                    bmove[i] = cc < a.I;
+                    col = c < 16 ? cc : a.I + cc;
+                } else {
+                    col = nt * BN + c * 8;
+                    bmove[i] = col < a.N;
+                }
+                bp[i] = bmove[i] ? W + (size_t)k * a.ldb + col : a.w.zeros + c * 8;
+            }
         }
+        bstep = MODE == ROWS_BK ? (long long)BK : (long long)BK * a.ldb;
 
         f32x16_t acc[4][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-        const int nsteps = a.K / BK;
-        uint4 va[8], vb[8];
-        load_kc(va, Arow, a.lda, mvalid, tid);
-        if (BMODE == B_NCONTIG) load_t(vb, Bsrc, a.ldb, BK, bok);
-        else load_kc(vb, Bsrc, a.ldb, bvalid, tid);
-        store_kc(va, As0, tid);
-        if (BMODE == B_NCONTIG) store_t(vb, Bs0, tid);
-        else store_kc(vb, Bs0, tid);
-        __syncthreads();
-        for (int s = 0; s < nsteps; ++s) {
-            const bool more = s + 1 < nsteps;
-            if (more) {
-                const int k0 = (s + 1) * BK;
-                load_kc(va, Arow + k0, a.lda, mvalid, tid);
-                if (BMODE == B_NCONTIG) load_t(vb, Bsrc + (size_t)k0 * a.ldb, a.ldb, BK, bok);
-                else load_kc(vb, Bsrc + k0, a.ldb, bvalid, tid);
-            }
-            const uint16_t* Ac = (s & 1) ? As1 : As0;
-            const uint16_t* Bc = (s & 1) ? Bs1 : Bs0;
-            mma_step<EPI>(acc, Ac, Bc, wm, wn, lane);
-            if (more) {
-                uint16_t* An = (s & 1) ? As0 : As1;
-                uint16_t* Bn = (s & 1) ? Bs0 : Bs1;
-                store_kc(va, An, tid);
-                if (BMODE == B_NCONTIG) store_t(vb, Bn, tid);
-                else store_kc(vb, Bn, tid);
-            }
-            __syncthreads();
-        }
-
-        epilogue_rows<EPI>(a, acc, smem, wm, wn, lane, nt, row0, mvalid);
+        zero_acc(acc);
+        pipeline<true, MODE == ROWS_BK, EPI>(acc, smem, nst, wm, wn, lane, [&](int s, int buf, int i) {
+            const uint32_t l = lds_wave + buf * STAGE_BYTES + i * 1024;
+            dma16(ap[i] + (size_t)s * BK, l);
+            dma16(bmove[i] ? bp[i] + (size_t)s * bstep : bp[i], l + OP_BYTES);
+        });
+        epi_rows_quarter<EPI, 0>(a, acc, ep, wm, wn, lane, nt, row0, mvalid);
+        epi_rows_quarter<EPI, 1>(a, acc, ep, wm, wn, lane, nt, row0, mvalid);
+        epi_rows_quarter<EPI, 2>(a, acc, ep, wm, wn, lane, nt, row0, mvalid);
+        epi_rows_quarter<EPI, 3>(a, acc, ep, wm, wn, lane, nt, row0, mvalid);
+        block_sync();   // the ring is reused by the next tile's loads
     }
 }
 
 // ---------------------------------------------------------------------------
-// Weight-gradient GEMM: dW[M, N] += A^T B over the target's row segments, where
-// A = [rows, M] and B = [rows, N] are both read row-major and transposed in registers.
-// Targets: t < E home expert t (home rows + its fallback replicas), else slot t - E.
+// Weight-gradient GEMM: dW[M, N] += A^T B over the target's row segments, where A = [rows, M]
+// and B = [rows, N] are read m/n-contiguous.  Targets: t < E is home expert t (its home rows
+// plus its fallback replicas, in plan order), t >= E is prefetch slot t - E.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256, 1) void gemm_dw_kernel(GemmArgs a) {
-    extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    __shared__ Segment s_seg[kMaxR + 1];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const PlanWs& w = a.w;
@@ -443,99 +517,82 @@ __global__ __launch_bounds__(256, 1) void gemm_dw_kernel(GemmArgs a) {
     const int xcd = blockIdx.x % nxcd, li = blockIdx.x / nxcd, per_wg = gridDim.x / nxcd;
     const int chunk = (total + nxcd - 1) / nxcd;
     const int t_lo = xcd * chunk, t_hi = min(total, t_lo + chunk);
-
-    uint16_t* As0 = smem;
-    uint16_t* Bs0 = smem + TILE_ELEMS;
-    uint16_t* As1 = smem + 2 * TILE_ELEMS;
-    uint16_t* Bs1 = smem + 3 * TILE_ELEMS;
+    float* ep = reinterpret_cast<float*>(smem) + wave * 32 * EPL;
+    const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds_addr(smem) + wave * 4 * 1024);
 
     for (int t = t_lo + li; t < t_hi; t += per_wg) {
         const int target = t / per_target;
         const int local = t % per_target;
         const int nt = local / MT, mt = local % MT;
-        // row segments of this target: home rows then fallback replicas (home expert), or the slot's rows
         float* out;
-        Segment first{0, 0};
-        const Segment* extra = nullptr;   // further segments (fallback replicas), read from the plan
         int nseg = 0;
         if (target < w.E) {
-            first = w.home_seg[target];
-            extra = w.fb_seg + (size_t)target * kMaxR;
-            if (!seg_ok(first, w)) first.rows = 0;
-            nseg = (first.rows > 0 ? 1 : 0) + min(max(w.fb_n[target], 0), kMaxR - 1);
-            if (first.rows == 0) {
-                first = extra[0];
-                ++extra;
+            const Segment hs = w.home_seg[target];
+            const int nfb = min(max(w.fb_n[target], 0), kMaxR - 1);
+            const bool has_home = seg_ok(hs, w) && hs.rows > 0;
+            nseg = (has_home ? 1 : 0) + nfb;
+            if (tid == 0 && has_home) s_seg[0] = hs;
+            if (tid >= 1 && tid <= nfb) {
+                const Segment f = w.fb_seg[(size_t)target * kMaxR + tid - 1];
+                s_seg[(has_home ? 1 : 0) + tid - 1] = seg_ok(f, w) ? f : Segment{0, 0};
             }
             out = a.dw_home + (size_t)target * a.M * a.N;
         } else {
             const int sl = target - w.E;
             if (w.slot_e[sl] < 0) continue;
-            first = Segment{w.slot_row0[sl], w.slot_rows[sl]};
-            if (!seg_ok(first, w)) continue;
+            const Segment f{w.slot_row0[sl], w.slot_rows[sl]};
+            if (!seg_ok(f, w)) continue;
+            if (tid == 0) s_seg[0] = f;
             nseg = 1;
             out = a.dw_slot + (size_t)sl * a.M * a.N;
         }
-        auto seg_at = [&](int i) -> Segment {
-            const Segment sg = i == 0 ? first : extra[i - 1];
-            return seg_ok(sg, w) ? sg : Segment{0, 0};
-        };
-        int nsteps = 0;
-        for (int i = 0; i < nseg; ++i) nsteps += (seg_at(i).rows + BK - 1) / BK;
-        if (nsteps == 0) continue;
-
-        const int m0 = mt * BM, n0 = nt * BN;
-        const int cblk = (tid & 31) * 8;
-        const bool aok = m0 + cblk < a.M, bok = n0 + cblk < a.N;
-        const int kb8 = (tid >> 5) * 8;
-
-        f32x16_t acc[4][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-        // step iterator over segments
-        int si = 0, sk = 0;   // segment index, row offset inside it
-        uint4 va[8], vb[8];
-        Segment cur = first;
-        auto load_step = [&](int koff) {
-            const Segment sg = cur;
-            const int kvalid = min(BK, sg.rows - koff) - kb8;
-            const size_t r0 = (size_t)(sg.row0 + koff + kb8);
-            load_t(va, a.A + r0 * a.lda + (aok ? m0 + cblk : 0), a.lda, kvalid, aok);
-            load_t(vb, a.B + r0 * a.ldb + (bok ? n0 + cblk : 0), a.ldb, kvalid, bok);
-        };
-        auto advance = [&]() {
-            sk += BK;
-            if (sk >= cur.rows) {
-                ++si;
-                sk = 0;
-                if (si < nseg) cur = seg_at(si);
-            }
-        };
-        load_step(sk);
-        advance();
-        store_t(va, As0, tid);
-        store_t(vb, Bs0, tid);
         __syncthreads();
-        for (int s = 0; s < nsteps; ++s) {
-            const bool more = s + 1 < nsteps;
-            if (more) {
-                load_step(sk);
-                advance();
-            }
-            mma_step<EPI_ACC_F32>(acc, (s & 1) ? As1 : As0, (s & 1) ? Bs1 : Bs0, wm, wn, lane);
-            if (more) {
-                store_t(va, (s & 1) ? As0 : As1, tid);
-                store_t(vb, (s & 1) ? Bs0 : Bs1, tid);
-            }
+        int nst = 0;
+        for (int i = 0; i < nseg; ++i) nst += (s_seg[i].rows + BK - 1) / BK;
+        if (nst == 0) {
             __syncthreads();
+            continue;
         }
-
-        epilogue_dw(a, acc, smem, wm, wn, lane, out, m0, n0);
+        const int m0 = mt * BM, n0 = nt * BN;
+        int kk_i[4], ac[4], bc[4], zc[4];
+        bool aok[4], bok[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int p = (wave * 4 + i) * 64 + lane;
+            const int k = p >> 5, c = (p & 31) ^ ((k & 3) << 2);
+            kk_i[i] = k;
+            zc[i] = c * 8;
+            ac[i] = m0 + c * 8;
+            bc[i] = n0 + c * 8;
+            aok[i] = ac[i] < a.M;
+            bok[i] = bc[i] < a.N;
+        }
+        // issue cursor over the segments (runs NSTAGE-1 steps ahead of the compute)
+        int iseg = 0, ikoff = 0;
+        Segment icur = s_seg[0];
+        f32x16_t acc[4][4];
+        zero_acc(acc);
+        pipeline<false, false, EPI_ACC_F32>(acc, smem, nst, wm, wn, lane, [&](int, int buf, int i) {
+            const uint32_t l = lds_wave + buf * STAGE_BYTES + i * 1024;
+            const int kr = ikoff + kk_i[i];
+            const bool v = kr < icur.rows;
+            const size_t row = (size_t)(icur.row0 + kr);
+            dma16(v && aok[i] ? a.A + row * a.lda + ac[i] : w.zeros + zc[i], l);
+            dma16(v && bok[i] ? a.B + row * a.ldb + bc[i] : w.zeros + zc[i], l + OP_BYTES);
+            if (i == 3) {    // step issued: advance the cursor
+                ikoff += BK;
+                if (ikoff >= icur.rows) {
+                    ikoff = 0;
+                    ++iseg;
+                    if (iseg < nseg) icur = s_seg[iseg];
+                }
+            }
+        });
+        epi_dw_quarter<0>(a, acc, ep, wm, wn, lane, out, m0, n0);
+        epi_dw_quarter<1>(a, acc, ep, wm, wn, lane, out, m0, n0);
+        epi_dw_quarter<2>(a, acc, ep, wm, wn, lane, out, m0, n0);
+        epi_dw_quarter<3>(a, acc, ep, wm, wn, lane, out, m0, n0);
+        block_sync();
     }
 }
 
@@ -557,18 +614,18 @@ static bool set_smem(K kernel) {
                                hipFuncAttributeMaxDynamicSharedMemorySize, GEMM_SMEM) == hipSuccess;
 }
 
-static int launch_rows(int epi, int bmode, const GemmArgs& a, hipStream_t s) {
+static int launch_rows(int epi, int mode, const GemmArgs& a, hipStream_t s) {
     const int grid = (num_cus() / 8) * 8;
-#define MOONEP_ROWS(E_, B_)                                                         \
-    do {                                                                            \
-        static bool ok = set_smem(gemm_rows_kernel<E_, B_>);                        \
-        if (!ok) return MOONEP_EHIP;                                                \
-        hipLaunchKernelGGL((gemm_rows_kernel<E_, B_>), dim3(grid), dim3(256), GEMM_SMEM, s, a); \
+#define MOONEP_ROWS(M_, E_)                                                                    \
+    do {                                                                                       \
+        static bool ok = set_smem(gemm_rows_kernel<M_, E_>);                                   \
+        if (!ok) return MOONEP_EHIP;                                                           \
+        hipLaunchKernelGGL((gemm_rows_kernel<M_, E_>), dim3(grid), dim3(256), GEMM_SMEM, s, a); \
     } while (0)
-    if (epi == EPI_SWIGLU_FWD && bmode == B_NCONTIG) MOONEP_ROWS(EPI_SWIGLU_FWD, B_NCONTIG);
-    else if (epi == EPI_STORE && bmode == B_NCONTIG) MOONEP_ROWS(EPI_STORE, B_NCONTIG);
-    else if (epi == EPI_SWIGLU_BWD && bmode == B_KCONTIG) MOONEP_ROWS(EPI_SWIGLU_BWD, B_KCONTIG);
-    else if (epi == EPI_STORE && bmode == B_KCONTIG) MOONEP_ROWS(EPI_STORE, B_KCONTIG);
+    if (epi == EPI_SWIGLU_FWD && mode == ROWS_BN) MOONEP_ROWS(ROWS_BN, EPI_SWIGLU_FWD);
+    else if (epi == EPI_STORE && mode == ROWS_BN) MOONEP_ROWS(ROWS_BN, EPI_STORE);
+    else if (epi == EPI_SWIGLU_BWD && mode == ROWS_BK) MOONEP_ROWS(ROWS_BK, EPI_SWIGLU_BWD);
+    else if (epi == EPI_STORE && mode == ROWS_BK) MOONEP_ROWS(ROWS_BK, EPI_STORE);
     else return MOONEP_ENOTSUP;
 #undef MOONEP_ROWS
     MOONEP_LAUNCH_CHECK();
@@ -588,7 +645,7 @@ static int check_ffn_dims(const moonep_dims_t* d) {
     int rc = check_dims(d, true);
     if (rc != MOONEP_OK) return rc;
     if (d->flags & MOONEP_F32_ROWS) return MOONEP_ENOTSUP;   // the expert GEMM is bf16
-    if (d->H % BK != 0 || d->I % BK != 0) return MOONEP_ENOTSUP;
+    if (d->H % 64 != 0 || d->I % 64 != 0) return MOONEP_ENOTSUP;
     return MOONEP_OK;
 }
 
@@ -632,7 +689,7 @@ extern "C" int moonep_grouped_ffn(const moonep_dims_t* dims, const void* plan_ws
     a.ldo = I;
     a.gu = static_cast<uint16_t*>(gu_save);
     a.ntiles_n = (I + 127) / 128;
-    rc = launch_rows(EPI_SWIGLU_FWD, B_NCONTIG, a, s);
+    rc = launch_rows(EPI_SWIGLU_FWD, ROWS_BN, a, s);
     if (rc != MOONEP_OK) return rc;
     // y = act W2
     a.A = static_cast<const uint16_t*>(act);
@@ -647,7 +704,7 @@ extern "C" int moonep_grouped_ffn(const moonep_dims_t* dims, const void* plan_ws
     a.ldo = H;
     a.gu = nullptr;
     a.ntiles_n = (H + BN - 1) / BN;
-    return launch_rows(EPI_STORE, B_NCONTIG, a, s);
+    return launch_rows(EPI_STORE, ROWS_BN, a, s);
 }
 
 extern "C" int moonep_grouped_ffn_backward(const moonep_dims_t* dims, const void* plan_ws,
@@ -692,7 +749,7 @@ extern "C" int moonep_grouped_ffn_backward(const moonep_dims_t* dims, const void
     a.I = I;
     a.gu = gu;
     a.ntiles_n = (I + BN - 1) / BN;
-    rc = launch_rows(EPI_SWIGLU_BWD, B_KCONTIG, a, s);
+    rc = launch_rows(EPI_SWIGLU_BWD, ROWS_BK, a, s);
     if (rc != MOONEP_OK) return rc;
     // dX = [dGt dU] W13^T (B = W13 [H, 2I] is k-contiguous)
     a.A = gu;
@@ -707,7 +764,7 @@ extern "C" int moonep_grouped_ffn_backward(const moonep_dims_t* dims, const void
     a.ldo = H;
     a.gu = nullptr;
     a.ntiles_n = (H + BN - 1) / BN;
-    rc = launch_rows(EPI_STORE, B_KCONTIG, a, s);
+    rc = launch_rows(EPI_STORE, ROWS_BK, a, s);
     if (rc != MOONEP_OK) return rc;
     // dW2 = A^T dY  ([I, H])
     GemmArgs d{};

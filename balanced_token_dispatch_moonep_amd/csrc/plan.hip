@@ -321,6 +321,8 @@ __global__ __launch_bounds__(256) void plan_decide(PlanWs w, uint32_t flags, int
         }
         w.ninst[e] = n;
     }
+    // zero row segment read by masked GEMM tile loads
+    for (int i = tid; i < kZeroElems / 2; i += 256) reinterpret_cast<uint32_t*>(w.zeros)[i] = 0u;
     // slot tables
     for (int i = tid; i < R * B; i += 256) {
         w.slot_e[i] = -1;
