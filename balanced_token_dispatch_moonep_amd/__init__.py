@@ -16,7 +16,7 @@ import os
 from typing import Optional
 
 __all__ = [
-    "MoonEPError", "Dims", "LIB_PATH", "lib", "NSTATS", "STAT_NAMES", "TRAINING", "F32_ROWS",
+    "MoonEPError", "Dims", "LIB_PATH", "lib", "NSTATS", "STAT_NAMES", "TRAINING", "F32_ROWS", "GRAD_ACCUM",
     "ST_BAD_ID", "ST_DUP_ID", "ST_CAPACITY", "ST_OVERFLOW", "ST_TRAIN_FALLBACK",
     "moonep_plan_workspace_bytes", "moonep_plan", "moonep_prefetch", "moonep_dispatch",
     "moonep_combine", "moonep_grouped_ffn", "moonep_grouped_ffn_backward", "moonep_reduce_grad",
@@ -27,6 +27,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoonep.s
 
 TRAINING = 1
 F32_ROWS = 2
+GRAD_ACCUM = 4
 NSTATS = 16
 ST_BAD_ID, ST_DUP_ID, ST_CAPACITY, ST_OVERFLOW, ST_TRAIN_FALLBACK = 1, 2, 4, 8, 16
 STAT_NAMES = (
@@ -55,8 +56,9 @@ class Dims(ctypes.Structure):
                 ("I", ctypes.c_int32), ("flags", ctypes.c_uint32)]
 
     @classmethod
-    def make(cls, R, E, B, S, K, H, I=0, training=False, f32_rows=False) -> "Dims":
-        return cls(R, E, B, S, K, H, I, (TRAINING if training else 0) | (F32_ROWS if f32_rows else 0))
+    def make(cls, R, E, B, S, K, H, I=0, training=False, f32_rows=False, grad_accum=False) -> "Dims":
+        flags = (TRAINING if training else 0) | (F32_ROWS if f32_rows else 0) | (GRAD_ACCUM if grad_accum else 0)
+        return cls(R, E, B, S, K, H, I, flags)
 
     @property
     def C(self) -> int:

@@ -63,7 +63,8 @@ struct PlanWs {
     int32_t* fb_n;         // [E] fallback replicas of expert e
     Segment* fb_seg;       // [E][kMaxR]
     Segment* home_seg;     // [E]
-    int32_t* counters;     // [64] scratch counters for persistent kernels
+    int32_t* counters;     // [64] tile counters of dynamically scheduled kernels
+    int32_t* dw_order;     // [E + R*B] dW targets by rows, descending (ties: lower id)
     uint16_t* zeros;       // [kZeroElems] zero bf16 row segment (source of masked GEMM tile loads)
 };
 
@@ -103,6 +104,7 @@ inline size_t plan_ws_layout(const moonep_dims_t* d, void* base, PlanWs* ws) {
     w.fb_seg = (Segment*)take(E * kMaxR * sizeof(Segment));
     w.home_seg = (Segment*)take(E * sizeof(Segment));
     w.counters = (int32_t*)take(64 * 4);
+    w.dw_order = (int32_t*)take((E + RB) * 4);
     w.zeros = (uint16_t*)take(kZeroElems * 2);
     (void)R;
     if (ws) *ws = w;
@@ -119,7 +121,7 @@ inline int check_dims(const moonep_dims_t* d, bool need_ffn) {
     if (d->S < 1 || d->K < 1 || d->K > kMaxK || d->K > d->E) return MOONEP_EINVAL;
     if ((int64_t)d->R * d->S * d->K > (int64_t)1 << 30) return MOONEP_EINVAL;
     if (d->H < 8 || d->H % 8 != 0) return MOONEP_EINVAL;
-    if (d->flags & ~(MOONEP_TRAINING | MOONEP_F32_ROWS)) return MOONEP_EINVAL;
+    if (d->flags & ~(MOONEP_TRAINING | MOONEP_F32_ROWS | MOONEP_GRAD_ACCUM)) return MOONEP_EINVAL;
     if (need_ffn && (d->I < 8 || d->I % 8 != 0)) return MOONEP_EINVAL;
     return MOONEP_OK;
 }

@@ -68,6 +68,8 @@ struct GemmArgs {
     float* dw_home;           // EPI_ACC_F32: [E, M, N]
     float* dw_slot;           // EPI_ACC_F32: [R*B, M, N]
     int ntiles_n;
+    int* counter;             // dW: tile counter (zero at launch)
+    int accum;                // dW: add into the outputs (1) or write them (0)
 };
 
 // ---------------------------------------------------------------------------
@@ -207,7 +209,9 @@ __device__ __forceinline__ void zero_acc(f32x16_t (&acc)[4][4]) {
 template <bool A_KC, bool B_KC, int EPI, typename Issue>
 __device__ __forceinline__ void pipeline(f32x16_t (&acc)[4][4], char* smem, int nst, int wm, int wn, int lane,
                                          Issue&& issue) {
-    wait_vm<0>();     // previous tile's epilogue stores are older than this tile's DMA
+    // No wait for the previous tile's epilogue stores: every vmcnt wait below bounds the number of
+    // outstanding operations, and loads complete in order among themselves, so "at most n
+    // outstanding" still means all but the last n DMA loads have landed.
 #pragma unroll
     for (int s = 0; s < NSTAGE - 1; ++s)
         if (s < nst)
@@ -357,6 +361,18 @@ __device__ __forceinline__ void epi_dw_quarter(const GemmArgs& a, const f32x16_t
     wave_sync();
     const int c = (lane & 31) * 4;
     const int col = n0 + wn * 128 + c;
+    if (!a.accum) {
+#pragma unroll
+        for (int it = 0; it < 16; ++it) {
+            const int rr = it * 2 + (lane >> 5);
+            const int row = m0 + wm * 128 + q * 32 + rr;
+            if (row < a.M && col < a.N)
+                *reinterpret_cast<float4*>(out + (size_t)row * a.N + col) =
+                    *reinterpret_cast<const float4*>(ep + rr * EPL + c);
+        }
+        wave_sync();
+        return;
+    }
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
         // all loads first (clamped to in-bounds addresses), then add and masked stores
@@ -506,22 +522,24 @@ __global__ __launch_bounds__(256, 1) void gemm_rows_kernel(GemmArgs a) {
 __global__ __launch_bounds__(256, 1) void gemm_dw_kernel(GemmArgs a) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     __shared__ Segment s_seg[kMaxR + 1];
+    __shared__ int s_tile[2];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const PlanWs& w = a.w;
     const int MT = (a.M + BM - 1) / BM, NT = a.ntiles_n;
     const int per_target = MT * NT;
-    const int ntargets = w.E + w.R * w.B;
-    const int total = ntargets * per_target;
-    const int nxcd = 8;
-    const int xcd = blockIdx.x % nxcd, li = blockIdx.x / nxcd, per_wg = gridDim.x / nxcd;
-    const int chunk = (total + nxcd - 1) / nxcd;
-    const int t_lo = xcd * chunk, t_hi = min(total, t_lo + chunk);
+    const int total = (w.E + w.R * w.B) * per_target;
     float* ep = reinterpret_cast<float*>(smem) + wave * 32 * EPL;
     const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds_addr(smem) + wave * 4 * 1024);
 
-    for (int t = t_lo + li; t < t_hi; t += per_wg) {
-        const int target = t / per_target;
+    // tiles are handed out dynamically, targets in descending row order (largest first)
+    for (int iter = 0;; ++iter) {
+        if (tid == 0) s_tile[iter & 1] = atomicAdd(a.counter, 1);
+        wait_lgkm0();
+        block_sync();
+        const int t = s_tile[iter & 1];
+        if (t >= total) break;
+        const int target = w.dw_order[t / per_target];
         const int local = t % per_target;
         const int nt = local / MT, mt = local % MT;
         float* out;
@@ -546,54 +564,60 @@ __global__ __launch_bounds__(256, 1) void gemm_dw_kernel(GemmArgs a) {
             nseg = 1;
             out = a.dw_slot + (size_t)sl * a.M * a.N;
         }
-        __syncthreads();
+        wait_lgkm0();
+        block_sync();
         int nst = 0;
         for (int i = 0; i < nseg; ++i) nst += (s_seg[i].rows + BK - 1) / BK;
-        if (nst == 0) {
-            __syncthreads();
-            continue;
-        }
         const int m0 = mt * BM, n0 = nt * BN;
-        int kk_i[4], ac[4], bc[4], zc[4];
-        bool aok[4], bok[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int p = (wave * 4 + i) * 64 + lane;
-            const int k = p >> 5, c = (p & 31) ^ ((k & 3) << 2);
-            kk_i[i] = k;
-            zc[i] = c * 8;
-            ac[i] = m0 + c * 8;
-            bc[i] = n0 + c * 8;
-            aok[i] = ac[i] < a.M;
-            bok[i] = bc[i] < a.N;
-        }
-        // issue cursor over the segments (runs NSTAGE-1 steps ahead of the compute)
-        int iseg = 0, ikoff = 0;
-        Segment icur = s_seg[0];
         f32x16_t acc[4][4];
         zero_acc(acc);
-        pipeline<false, false, EPI_ACC_F32>(acc, smem, nst, wm, wn, lane, [&](int, int buf, int i) {
-            const uint32_t l = lds_wave + buf * STAGE_BYTES + i * 1024;
-            const int kr = ikoff + kk_i[i];
-            const bool v = kr < icur.rows;
-            const size_t row = (size_t)(icur.row0 + kr);
-            dma16(v && aok[i] ? a.A + row * a.lda + ac[i] : w.zeros + zc[i], l);
-            dma16(v && bok[i] ? a.B + row * a.ldb + bc[i] : w.zeros + zc[i], l + OP_BYTES);
-            if (i == 3) {    // step issued: advance the cursor
-                ikoff += BK;
-                if (ikoff >= icur.rows) {
-                    ikoff = 0;
-                    ++iseg;
-                    if (iseg < nseg) icur = s_seg[iseg];
-                }
+        if (nst > 0) {
+            int kk_i[4], ac[4], bc[4], zc[4];
+            bool aok[4], bok[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int p = (wave * 4 + i) * 64 + lane;
+                const int k = p >> 5, c = (p & 31) ^ ((k & 3) << 2);
+                kk_i[i] = k;
+                zc[i] = c * 8;
+                ac[i] = m0 + c * 8;
+                bc[i] = n0 + c * 8;
+                aok[i] = ac[i] < a.M;
+                bok[i] = bc[i] < a.N;
             }
-        });
+            // issue cursor over the segments (runs NSTAGE-1 steps ahead of the compute)
+            int iseg = 0, ikoff = 0;
+            Segment icur = s_seg[0];
+            pipeline<false, false, EPI_ACC_F32>(acc, smem, nst, wm, wn, lane, [&](int, int buf, int i) {
+                const uint32_t l = lds_wave + buf * STAGE_BYTES + i * 1024;
+                const int kr = ikoff + kk_i[i];
+                const bool v = kr < icur.rows;
+                const size_t row = (size_t)(icur.row0 + kr);
+                dma16(v && aok[i] ? a.A + row * a.lda + ac[i] : w.zeros + zc[i], l);
+                dma16(v && bok[i] ? a.B + row * a.ldb + bc[i] : w.zeros + zc[i], l + OP_BYTES);
+                if (i == 3) {    // step issued: advance the cursor
+                    ikoff += BK;
+                    if (ikoff >= icur.rows) {
+                        ikoff = 0;
+                        ++iseg;
+                        if (iseg < nseg) icur = s_seg[iseg];
+                    }
+                }
+            });
+        } else if (a.accum) {
+            continue;           // nothing to add
+        }
+        // (an expert without rows gets a zero gradient when the outputs are written)
         epi_dw_quarter<0>(a, acc, ep, wm, wn, lane, out, m0, n0);
         epi_dw_quarter<1>(a, acc, ep, wm, wn, lane, out, m0, n0);
         epi_dw_quarter<2>(a, acc, ep, wm, wn, lane, out, m0, n0);
         epi_dw_quarter<3>(a, acc, ep, wm, wn, lane, out, m0, n0);
         block_sync();
     }
+}
+
+__global__ void reset_counters_kernel(int* c, int n) {
+    if ((int)threadIdx.x < n) c[threadIdx.x] = 0;
 }
 
 static int g_num_cu = 0;
@@ -737,6 +761,9 @@ extern "C" int moonep_grouped_ffn_backward(const moonep_dims_t* dims, const void
     GemmArgs a{};
     plan_ws_layout(dims, const_cast<void*>(plan_ws), &a.w);
     uint16_t* gu = static_cast<uint16_t*>(const_cast<void*>(gu_save));
+    // tile counters of the two weight-gradient launches
+    hipLaunchKernelGGL(reset_counters_kernel, dim3(1), dim3(64), 0, s, a.w.counters, 2);
+    MOONEP_LAUNCH_CHECK();
     // dA = dY W2^T (B = W2 [I, H] is k-contiguous), fused SwiGLU' written over Gt|U
     a.A = static_cast<const uint16_t*>(dy);
     a.lda = H;
@@ -778,6 +805,8 @@ extern "C" int moonep_grouped_ffn_backward(const moonep_dims_t* dims, const void
     d.dw_home = dw2_home;
     d.dw_slot = dw2_red;
     d.ntiles_n = (H + BN - 1) / BN;
+    d.counter = a.w.counters;
+    d.accum = (dims->flags & MOONEP_GRAD_ACCUM) ? 1 : 0;
     rc = launch_dw(d, s);
     if (rc != MOONEP_OK) return rc;
     // dW13 = X^T [dGt dU]  ([H, 2I])
@@ -790,5 +819,6 @@ extern "C" int moonep_grouped_ffn_backward(const moonep_dims_t* dims, const void
     d.dw_home = dw13_home;
     d.dw_slot = dw13_red;
     d.ntiles_n = (2 * I + BN - 1) / BN;
+    d.counter = a.w.counters + 1;
     return launch_dw(d, s);
 }

@@ -112,7 +112,7 @@ struct DecideShared {
     int don[kMaxR], rec[kMaxR];
     int nd, nr, nent, status, ngroups;
     int rank_nent[kMaxR];
-    int red[8];
+    int trows[kMaxE + kMaxR * kMaxB];   // rows of each dW target
 };
 
 __global__ __launch_bounds__(256) void plan_decide(PlanWs w, uint32_t flags, int32_t* __restrict__ cu,
@@ -365,6 +365,33 @@ __global__ __launch_bounds__(256) void plan_decide(PlanWs w, uint32_t flags, int
     // entries table (for inspection)
     for (int i = tid; i < nent; i += 256)
         for (int f = 0; f < 5; ++f) w.entries[i * 5 + f] = sh.ent[i][f];
+    // dW targets (home experts with their fallback replicas, then slots) by rows, descending:
+    // the weight-gradient GEMM hands out the largest first (longest-processing-time order)
+    const int ntarget = E + R * B;
+    for (int t = tid; t < ntarget; t += 256) {
+        int rows = 0;
+        if (ok) {
+            if (t < E) {
+                rows = sh.avail[t];
+                for (int i = 0; i < nent; ++i)
+                    if (sh.ent[i][0] == t && sh.ent[i][4] < E) rows += sh.ent[i][2];
+            } else {
+                for (int i = 0; i < nent; ++i)
+                    if (sh.ent[i][4] >= E && sh.ent[i][1] * B + sh.ent[i][3] == t - E) rows = sh.ent[i][2];
+            }
+        }
+        sh.trows[t] = rows;
+    }
+    __syncthreads();
+    for (int t = tid; t < ntarget; t += 256) {
+        const int r = sh.trows[t];
+        int rank = 0;
+        for (int u = 0; u < ntarget; ++u) {
+            const int v = sh.trows[u];
+            rank += (v > r) || (v == r && u < t);
+        }
+        w.dw_order[rank] = t;
+    }
     __syncthreads();
 
     if (tid == 0) {

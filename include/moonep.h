@@ -56,11 +56,12 @@ typedef struct moonep_dims {
     int32_t K;       /* experts per token, 1..min(E, 16)                            */
     int32_t H;       /* hidden size, multiple of 8                                  */
     int32_t I;       /* SwiGLU intermediate size, multiple of 8 (0 if no expert FFN) */
-    uint32_t flags;  /* MOONEP_TRAINING | MOONEP_F32_ROWS                          */
+    uint32_t flags;  /* MOONEP_TRAINING | MOONEP_F32_ROWS | MOONEP_GRAD_ACCUM      */
 } moonep_dims_t;
 
 #define MOONEP_TRAINING 1u   /* plan for training: a fallback replica sets MOONEP_ST_TRAIN_FALLBACK */
 #define MOONEP_F32_ROWS 2u   /* dispatch/combine rows are float32 instead of bf16 */
+#define MOONEP_GRAD_ACCUM 4u /* grouped_ffn_backward adds into dw*_home / dw*_red instead of writing them */
 
 enum {
     MOONEP_OK = 0,
@@ -96,7 +97,9 @@ size_t moonep_plan_workspace_bytes(const moonep_dims_t* dims);
  * router output -> planning kernel; AL, How it works; TD, memory contract].
  *   topk       [R, S, K] int32  expert ids chosen by the router for each token (k order kept)
  *   plan_ws    workspace of moonep_plan_workspace_bytes() bytes; stays valid (and is read by
- *              prefetch / grouped_ffn / reduce_grad) until the next moonep_plan on it
+ *              prefetch / grouped_ffn / reduce_grad) until the next moonep_plan on it.
+ *              grouped_ffn_backward also uses two words of it as tile counters, so two
+ *              backward calls on one workspace must not run concurrently.
  *   cu_seqlens [R, E+B+1] int32 out: per rank, prefix sums of the rows served by each weight
  *              row (home rows [0,E), slot rows [E,E+B)); cu_seqlens[q][E+B] == S*K
  *   dest       [R, S, K] int32 out: absolute row in the [R*S*K] receive buffer where the
@@ -153,14 +156,19 @@ int moonep_grouped_ffn(const moonep_dims_t* dims, const void* plan_ws, const int
  * dU = dA silu(Gt); dX = [dGt dU] W13^T; dW2 = A^T dY; dW13 = X^T [dGt dU].
  * Weight gradients of slot replicas go to the separate fp32 reduce buffers (they must not
  * reach the framework's gradient reduction [TD, memory contract; AT, Technical Details]);
- * home experts accumulate into dw*_home.  A fallback replica (training with B < E/R, an
- * extension: the pages ask for B = E/R in training) accumulates into its home expert's
- * gradient together with the home rows.
+ * home experts' gradients go to dw*_home.  A fallback replica (training with B < E/R, an
+ * extension: the pages ask for B = E/R in training) contributes to its home expert's gradient
+ * together with the home rows.
  *   dy        [R*S*K, H] bf16 upstream gradient of y (e.g. moonep_dispatch with row_scale)
+ *   gu_save   in: Gt|U from moonep_grouped_ffn; out: overwritten with dGt|dU
  *   drecv     [R*S*K, H] bf16 out
- *   dw13_home [E, H, 2I] float32, dw2_home [E, I, H] float32: accumulated (+=)
- *   dw13_red  [R, B, H, 2I] float32, dw2_red [R, B, I, H] float32: accumulated (+=); the
- *             slots are zero at the start of a step (moonep_reduce_grad clears them) */
+ *   dw13_home [E, H, 2I] float32, dw2_home [E, I, H] float32: every expert's gradient of this call
+ *   dw13_red  [R, B, H, 2I] float32, dw2_red [R, B, I, H] float32: the gradient of each slot
+ *             replica of this call (slots without a replica are untouched)
+ *   Without MOONEP_GRAD_ACCUM the gradients are written (each home expert, including experts
+ *   that received no rows, and each used slot); with it they are added to what the buffers
+ *   hold (e.g. accumulation over micro-batches; the reduce slots are zero after
+ *   moonep_reduce_grad). */
 int moonep_grouped_ffn_backward(const moonep_dims_t* dims, const void* plan_ws,
                                 const int32_t* cu_seqlens, const void* recv,
                                 const void* gu_save, const void* act, const void* dy,

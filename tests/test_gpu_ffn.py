@@ -116,19 +116,33 @@ def test_backward_mid(B):
     assert rel_fro(g13, rdW13) <= TOL and rel_fro(g2, rdW2) <= TOL
 
 
-def test_backward_accumulates():
-    """Two backward passes on the same batch double the home gradients; reduce buffers stay clean."""
-    topk, gates, xb, wb13, wb2, d, plan, dest, layer = _setup(MID, training=True)
-    dout = bf16_from_bits(W.grad_rows(MID.R, MID.S, MID.H, 7, "bf16"))
-    x, tk, g = bf16_from_bits(xb), i32(topk), f32(gates)
-    layer.forward(x, tk, g)
-    layer.backward(dout, g)
-    one13 = layer.dw13.clone()
-    layer.forward(x, tk, g)
-    layer.backward(dout, g)
-    torch.cuda.synchronize()
-    assert rel_fro(f64_of(layer.dw13), 2 * f64_of(one13)) <= 1e-6
-    assert not layer.dw13_red.any()
+def test_backward_writes_or_accumulates():
+    """Without MOONEP_GRAD_ACCUM a second backward on the same batch rewrites the same
+    gradients; with it the home gradients double.  Reduce buffers are clean after each step."""
+    for accum in (False, True):
+        topk, gates, _ = W.routing_for(MID)
+        xb = W.hidden_rows(MID.R, MID.S, MID.H, MID.seed, "bf16")
+        w13f, w2f = W.expert_weights_np(MID.E, MID.H, MID.I, MID.seed)
+        d = M.Dims.make(MID.R, MID.E, MID.B, MID.S, MID.K, MID.H, MID.I, training=True, grad_accum=accum)
+        layer = MoonEPLayer(d, w13=bf16_from_bits(W.bf16_bits(w13f)), w2=bf16_from_bits(W.bf16_bits(w2f)),
+                            training=True)
+        dout = bf16_from_bits(W.grad_rows(MID.R, MID.S, MID.H, 7, "bf16"))
+        x, tk, g = bf16_from_bits(xb), i32(topk), f32(gates)
+        layer.dw13.fill_(3.0)        # stale content: must be overwritten unless accumulating
+        layer.forward(x, tk, g)
+        layer.backward(dout, g)
+        one13 = layer.dw13.clone()
+        one2 = layer.dw2.clone()
+        layer.forward(x, tk, g)
+        layer.backward(dout, g)
+        torch.cuda.synchronize()
+        if accum:
+            ref = f64_of(one13) - 3.0
+            assert rel_fro(f64_of(layer.dw13) - 3.0, 2 * ref) <= 1e-6
+        else:
+            assert torch.equal(layer.dw13, one13) and torch.equal(layer.dw2, one2)
+            assert not bool((layer.dw13 == 3.0).any())
+        assert not layer.dw13_red.any()
 
 
 def test_tiny_layer_f32_rows():
