@@ -44,9 +44,8 @@ constexpr int BM = 256, BN = 256, BK = 32, NSTAGE = 4;
 constexpr int OP_BYTES = 256 * BK * 2;             // one operand tile of one stage: 16 KiB
 constexpr int STAGE_BYTES = 2 * OP_BYTES;
 constexpr int GEMM_SMEM = NSTAGE * STAGE_BYTES;    // 128 KiB
-constexpr int EPL = 132;                           // fp32 pitch of a staged epilogue row
 constexpr int MAX_GROUPS = 2 * kMaxE;
-static_assert(4 * 32 * EPL * 4 <= GEMM_SMEM, "epilogue staging must fit in the stage ring");
+static_assert(4 * 32 * 132 * 4 <= GEMM_SMEM, "epilogue staging must fit in the stage ring");
 
 enum Epi { EPI_SWIGLU_FWD = 0, EPI_STORE = 1, EPI_SWIGLU_BWD = 2, EPI_ACC_F32 = 3 };
 enum Mode { ROWS_BN = 0, ROWS_BK = 1 };   // weights n-contiguous ([K, N]) or k-contiguous ([N, K])
@@ -143,38 +142,58 @@ __device__ __forceinline__ bf16x8_t frag_mn(const char* T, int mb, int kk, int l
     return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// LDS column (tile n index) of wave-local MFMA column tile tj.
-template <int EPI>
-__device__ __forceinline__ int bcol(int wn, int tj) {
-    if (EPI == EPI_SWIGLU_FWD) return tj < 2 ? wn * 64 + tj * 32 : 128 + wn * 64 + (tj - 2) * 32;
-    return wn * 128 + tj * 32;
-}
-
-// MFMA operand fragments of one 16-k slice of a stage: 4 row tiles of A, 4 column tiles of B.
-struct Frags {
-    bf16x8_t a[4], b[4];
+// Wave layout of a 256x256 tile: 2 x WN waves; wave (wm, wn) owns rows wm*128 .. +128 and
+// TN = 8/WN column blocks of 32.  WN = 2: 4 waves of 128x128 (one per SIMD); WN = 4: 8 waves of
+// 128x64 (two per SIMD, so one wave's MFMAs cover the other's memory waits).
+template <int WN>
+struct WL {
+    static constexpr int WAVES = 2 * WN;
+    static constexpr int NTHR = 64 * WAVES;
+    static constexpr int TN = 8 / WN;                  // 32-column blocks per wave
+    static constexpr int PARTS = 16 / WAVES;           // DMA loads per operand, step and wave
+    static constexpr int PER_STEP = 2 * PARTS;         // DMA loads per step and wave
+    static constexpr int EPL = TN * 32 + 4;            // fp32 pitch of a staged epilogue row
 };
 
-template <bool A_KC, bool B_KC, int EPI>
-__device__ __forceinline__ void load_frags(Frags& f, const char* st, int kk, int wm, int wn, int lane) {
+// LDS column (tile n index) of wave-local MFMA column block tj.
+template <int EPI, int WN>
+__device__ __forceinline__ int bcol(int wn, int tj) {
+    constexpr int TN = WL<WN>::TN;
+    if (EPI == EPI_SWIGLU_FWD) {   // tile columns [0,128) gate, [128,256) up; a wave gets both halves
+        constexpr int half = TN / 2;
+        return tj < half ? wn * (128 / WN) + tj * 32 : 128 + wn * (128 / WN) + (tj - half) * 32;
+    }
+    return wn * (256 / WN) + tj * 32;
+}
+
+// MFMA operand fragments of one 16-k slice of a stage: 4 row blocks of A, TN column blocks of B.
+template <int TN>
+struct Frags {
+    bf16x8_t a[4], b[TN];
+};
+
+template <bool A_KC, bool B_KC, int EPI, int WN>
+__device__ __forceinline__ void load_frags(Frags<WL<WN>::TN>& f, const char* st, int kk, int wm, int wn, int lane) {
     const char* As = st;
     const char* Bs = st + OP_BYTES;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
         f.a[t] = A_KC ? frag_kc(As, wm * 128 + t * 32, kk, lane) : frag_mn(As, wm * 128 + t * 32, kk, lane);
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-        f.b[t] = B_KC ? frag_kc(Bs, bcol<EPI>(wn, t), kk, lane) : frag_mn(Bs, bcol<EPI>(wn, t), kk, lane);
+    for (int t = 0; t < WL<WN>::TN; ++t)
+        f.b[t] = B_KC ? frag_kc(Bs, bcol<EPI, WN>(wn, t), kk, lane) : frag_mn(Bs, bcol<EPI, WN>(wn, t), kk, lane);
 }
 
-__device__ __forceinline__ void mma_row(f32x16_t (&acc)[4][4], const Frags& f, int i) {
+template <int TN>
+__device__ __forceinline__ void mma_row(f32x16_t (&acc)[4][TN], const Frags<TN>& f, int i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < TN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
 }
-__device__ __forceinline__ void mma_frags(f32x16_t (&acc)[4][4], const Frags& f) {
+template <int TN>
+__device__ __forceinline__ void mma_frags(f32x16_t (&acc)[4][TN], const Frags<TN>& f) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) mma_row(acc, f, i);
+    for (int i = 0; i < 4; ++i) mma_row<TN>(acc, f, i);
 }
 
 __device__ __forceinline__ float sigm(float x) { return 1.0f / (1.0f + __expf(-x)); }
@@ -190,25 +209,28 @@ __device__ __forceinline__ bool seg_ok(const Segment& s, const PlanWs& w) {
     return s.row0 >= 0 && s.rows >= 0 && (long long)s.row0 + s.rows <= (long long)w.R * w.C;
 }
 
-__device__ __forceinline__ void zero_acc(f32x16_t (&acc)[4][4]) {
+template <int TN>
+__device__ __forceinline__ void zero_acc(f32x16_t (&acc)[4][TN]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 }
 
-// Main loop over nst K-steps of 32 (two 16-k slices each).  issue(s, buf, part) enqueues
-// this wave's DMA loads of step s (part p = one load per operand, p = 0..3) into a ring of
-// NSTAGE buffers.  Fragments are double-buffered in registers: the reads of the next slice are
-// issued before the MFMAs of the current one; the step barrier sits between a step's two slices
-// so the MFMAs already issued keep the matrix cores busy across it; and the DMA loads of step
-// s+3 are spread between the MFMAs of the second slice, so no burst of memory instructions
-// stalls the wave's in-order issue while the matrix pipe drains.
-template <bool A_KC, bool B_KC, int EPI, typename Issue>
-__device__ __forceinline__ void pipeline(f32x16_t (&acc)[4][4], char* smem, int nst, int wm, int wn, int lane,
-                                         Issue&& issue) {
+// Main loop over nst K-steps of 32 (two 16-k slices each).  issue(s, buf, part) enqueues this
+// wave's DMA loads of step s (one per operand for part p, p < PARTS) into a ring of NSTAGE
+// buffers.  Fragments are double-buffered in registers: the reads of the next slice are issued
+// before the MFMAs of the current one; the step barrier sits between a step's two slices so the
+// MFMAs already issued keep the matrix cores busy across it; and the DMA loads of step s+3 are
+// spread between the MFMAs of the second slice, so no burst of memory instructions stalls the
+// wave's in-order issue while the matrix pipe drains.
+template <bool A_KC, bool B_KC, int EPI, int WN, typename Issue>
+__device__ __forceinline__ void pipeline(f32x16_t (&acc)[4][WL<WN>::TN], char* smem, int nst, int wm, int wn,
+                                         int lane, Issue&& issue) {
+    using L = WL<WN>;
+    constexpr int PER = L::PER_STEP;
     // No wait for the previous tile's epilogue stores: every vmcnt wait below bounds the number of
     // outstanding operations, and loads complete in order among themselves, so "at most n
     // outstanding" still means all but the last n DMA loads have landed.
@@ -216,52 +238,52 @@ __device__ __forceinline__ void pipeline(f32x16_t (&acc)[4][4], char* smem, int 
     for (int s = 0; s < NSTAGE - 1; ++s)
         if (s < nst)
 #pragma unroll
-            for (int p = 0; p < 4; ++p) issue(s, s, p);
-    if (nst >= 3) wait_vm<16>();
-    else if (nst == 2) wait_vm<8>();
+            for (int p = 0; p < L::PARTS; ++p) issue(s, s, p);
+    if (nst >= 3) wait_vm<2 * PER>();
+    else if (nst == 2) wait_vm<PER>();
     else wait_vm<0>();
     block_sync();
-    Frags f0, f1;
-    load_frags<A_KC, B_KC, EPI>(f0, smem, 0, wm, wn, lane);
+    Frags<L::TN> f0, f1;
+    load_frags<A_KC, B_KC, EPI, WN>(f0, smem, 0, wm, wn, lane);
     for (int s = 0; s < nst; ++s) {
         const char* st = smem + (s & (NSTAGE - 1)) * STAGE_BYTES;
-        load_frags<A_KC, B_KC, EPI>(f1, st, 1, wm, wn, lane);
-        mma_frags(acc, f0);
+        load_frags<A_KC, B_KC, EPI, WN>(f1, st, 1, wm, wn, lane);
+        mma_frags<L::TN>(acc, f0);
         // slice-1 fragments were read long ago; settling them here keeps the compiler from making
         // the next MFMAs wait on the reads issued after the barrier
         wait_lgkm0();
         if (s + 1 < nst) {
             // step s+1 must have landed: only step s+2 may still be in flight
-            if (s + 2 < nst) wait_vm<8>();
+            if (s + 2 < nst) wait_vm<PER>();
             else wait_vm<0>();
             block_sync();
-            load_frags<A_KC, B_KC, EPI>(f0, smem + ((s + 1) & (NSTAGE - 1)) * STAGE_BYTES, 0, wm, wn, lane);
+            load_frags<A_KC, B_KC, EPI, WN>(f0, smem + ((s + 1) & (NSTAGE - 1)) * STAGE_BYTES, 0, wm, wn, lane);
         }
         // every wave is past step s-1, so its buffer takes step s+3
         const bool more = s + NSTAGE - 1 < nst;
         const int nb = (s + NSTAGE - 1) & (NSTAGE - 1);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            mma_row(acc, f1, i);
-            if (more) issue(s + NSTAGE - 1, nb, i);
+            mma_row<L::TN>(acc, f1, i);
+            if (more && i % (4 / L::PARTS) == 0) issue(s + NSTAGE - 1, nb, i / (4 / L::PARTS));
         }
     }
     block_sync();     // every wave is done with the ring before the epilogue reuses it
 }
 
 // ---------------------------------------------------------------------------
-// Epilogues: each wave stages a 32 x 128 fp32 quarter of its accumulators in its own LDS
+// Epilogues: each wave stages a 32-row quarter of its accumulators (fp32) in its own LDS
 // region, then every lane handles 8 (or 4) consecutive columns of a row so global accesses
 // are 16 bytes wide.  C layout of a 32x32 MFMA tile: lane l, reg r -> row (r/4)*8 + (l/32)*4
 // + r%4, column l%32.
 // ---------------------------------------------------------------------------
-template <int q>
-__device__ __forceinline__ void stage_quarter(const f32x16_t (&acc)[4][4], float* ep, int lane) {
+template <int q, int TN, int EPLD>
+__device__ __forceinline__ void stage_quarter(const f32x16_t (&acc)[4][TN], float* ep, int lane) {
     const int lc = lane & 31, lr4 = (lane >> 5) * 4;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) ep[((r >> 2) * 8 + lr4 + (r & 3)) * EPL + j * 32 + lc] = acc[q][j][r];
+        for (int r = 0; r < 16; ++r) ep[((r >> 2) * 8 + lr4 + (r & 3)) * EPLD + j * 32 + lc] = acc[q][j][r];
 }
 
 __device__ __forceinline__ uint4 pack8(const float (&v)[8]) {
@@ -277,24 +299,27 @@ __device__ __forceinline__ void read8(const float* p, float (&v)[8]) {
     v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w; v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
 }
 
-template <int EPI, int q>
-__device__ __forceinline__ void epi_rows_quarter(const GemmArgs& a, const f32x16_t (&acc)[4][4], float* ep, int wm,
-                                                 int wn, int lane, int nt, int row0, int mvalid) {
-    stage_quarter<q>(acc, ep, lane);
+template <int EPI, int WN, int q>
+__device__ __forceinline__ void epi_rows_quarter(const GemmArgs& a, const f32x16_t (&acc)[4][WL<WN>::TN], float* ep,
+                                                 int wm, int wn, int lane, int nt, int row0, int mvalid) {
+    constexpr int TN = WL<WN>::TN, EPLD = WL<WN>::EPL;
+    stage_quarter<q, TN, EPLD>(acc, ep, lane);
     wave_sync();
     const int rbase = wm * 128 + q * 32;   // tile-local row of the quarter's first row
     if (EPI == EPI_SWIGLU_FWD) {
-        // staged columns 0..63 = gate, 64..127 = up, for act columns nt*128 + wn*64 + c
+        // staged columns [0, 16 TN) = gate, [16 TN, 32 TN) = up, for act columns
+        // nt*128 + wn*(128/WN) + c; 2 TN lanes per row, 8 columns each
+        constexpr int LPR = 2 * TN, RPI = 64 / LPR;
         const int I = a.I;
-        const int c = (lane & 7) * 8;
-        const int col = nt * 128 + wn * 64 + c;
+        const int c = (lane % LPR) * 8;
+        const int col = nt * 128 + wn * (128 / WN) + c;
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int rr = it * 8 + (lane >> 3);
+        for (int it = 0; it < 32 / RPI; ++it) {
+            const int rr = it * RPI + lane / LPR;
             if (rbase + rr < mvalid && col < I) {
                 float g[8], u[8], o[8];
-                read8(ep + rr * EPL + c, g);
-                read8(ep + rr * EPL + 64 + c, u);
+                read8(ep + rr * EPLD + c, g);
+                read8(ep + rr * EPLD + 16 * TN + c, u);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) o[i] = g[i] * sigm(g[i]) * u[i];
                 const size_t row = (size_t)(row0 + rbase + rr);
@@ -306,26 +331,27 @@ __device__ __forceinline__ void epi_rows_quarter(const GemmArgs& a, const f32x16
             }
         }
     } else if (EPI == EPI_SWIGLU_BWD) {
+        constexpr int LPR = 4 * TN, RPI = 64 / LPR, IT = 32 / RPI;
         const int I = a.I;
-        const int c = (lane & 15) * 8;
-        const int col = nt * BN + wn * 128 + c;
+        const int c = (lane % LPR) * 8;
+        const int col = nt * BN + wn * (256 / WN) + c;
         // all loads first (clamped to in-bounds addresses), then compute and masked stores
-        uint4 gv[8], uv[8];
+        uint4 gv[IT], uv[IT];
         const int lcol = min(col, I - 8);
 #pragma unroll
-        for (int it = 0; it < 8; ++it) {
-            const int rr = it * 4 + (lane >> 4);
+        for (int it = 0; it < IT; ++it) {
+            const int rr = it * RPI + lane / LPR;
             const size_t row = (size_t)(row0 + min(rbase + rr, mvalid - 1));
             gv[it] = *reinterpret_cast<const uint4*>(a.gu + row * 2 * I + lcol);
             uv[it] = *reinterpret_cast<const uint4*>(a.gu + row * 2 * I + I + lcol);
         }
 #pragma unroll
-        for (int it = 0; it < 8; ++it) {
-            const int rr = it * 4 + (lane >> 4);
+        for (int it = 0; it < IT; ++it) {
+            const int rr = it * RPI + lane / LPR;
             if (rbase + rr < mvalid && col < I) {
                 const size_t row = (size_t)(row0 + rbase + rr);
                 float da[8], g[8], u[8], dg[8], du[8];
-                read8(ep + rr * EPL + c, da);
+                read8(ep + rr * EPLD + c, da);
                 unpack8(gv[it], g);
                 unpack8(uv[it], u);
 #pragma unroll
@@ -339,14 +365,15 @@ __device__ __forceinline__ void epi_rows_quarter(const GemmArgs& a, const f32x16
             }
         }
     } else {
-        const int c = (lane & 15) * 8;
-        const int col = nt * BN + wn * 128 + c;
+        constexpr int LPR = 4 * TN, RPI = 64 / LPR, IT = 32 / RPI;
+        const int c = (lane % LPR) * 8;
+        const int col = nt * BN + wn * (256 / WN) + c;
 #pragma unroll
-        for (int it = 0; it < 8; ++it) {
-            const int rr = it * 4 + (lane >> 4);
+        for (int it = 0; it < IT; ++it) {
+            const int rr = it * RPI + lane / LPR;
             if (rbase + rr < mvalid && col < a.N) {
                 float v[8];
-                read8(ep + rr * EPL + c, v);
+                read8(ep + rr * EPLD + c, v);
                 *reinterpret_cast<uint4*>(a.out + (size_t)(row0 + rbase + rr) * a.ldo + col) = pack8(v);
             }
         }
@@ -354,42 +381,44 @@ __device__ __forceinline__ void epi_rows_quarter(const GemmArgs& a, const f32x16
     wave_sync();
 }
 
-template <int q>
-__device__ __forceinline__ void epi_dw_quarter(const GemmArgs& a, const f32x16_t (&acc)[4][4], float* ep, int wm,
-                                               int wn, int lane, float* out, int m0, int n0) {
-    stage_quarter<q>(acc, ep, lane);
+template <int WN, int q>
+__device__ __forceinline__ void epi_dw_quarter(const GemmArgs& a, const f32x16_t (&acc)[4][WL<WN>::TN], float* ep,
+                                               int wm, int wn, int lane, float* out, int m0, int n0) {
+    constexpr int TN = WL<WN>::TN, EPLD = WL<WN>::EPL;
+    constexpr int LPR = 8 * TN, RPI = 64 / LPR, IT = 32 / RPI;   // float4 chunks
+    stage_quarter<q, TN, EPLD>(acc, ep, lane);
     wave_sync();
-    const int c = (lane & 31) * 4;
-    const int col = n0 + wn * 128 + c;
+    const int c = (lane % LPR) * 4;
+    const int col = n0 + wn * (256 / WN) + c;
     if (!a.accum) {
 #pragma unroll
-        for (int it = 0; it < 16; ++it) {
-            const int rr = it * 2 + (lane >> 5);
+        for (int it = 0; it < IT; ++it) {
+            const int rr = it * RPI + lane / LPR;
             const int row = m0 + wm * 128 + q * 32 + rr;
             if (row < a.M && col < a.N)
                 *reinterpret_cast<float4*>(out + (size_t)row * a.N + col) =
-                    *reinterpret_cast<const float4*>(ep + rr * EPL + c);
+                    *reinterpret_cast<const float4*>(ep + rr * EPLD + c);
         }
         wave_sync();
         return;
     }
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    for (int half = 0; half < IT / 8; ++half) {
         // all loads first (clamped to in-bounds addresses), then add and masked stores
         float4 old[8];
         const int lcol = min(col, a.N - 4);
 #pragma unroll
         for (int it = 0; it < 8; ++it) {
-            const int rr = (half * 8 + it) * 2 + (lane >> 5);
+            const int rr = (half * 8 + it) * RPI + lane / LPR;
             const int row = min(m0 + wm * 128 + q * 32 + rr, a.M - 1);
             old[it] = *reinterpret_cast<const float4*>(out + (size_t)row * a.N + lcol);
         }
 #pragma unroll
         for (int it = 0; it < 8; ++it) {
-            const int rr = (half * 8 + it) * 2 + (lane >> 5);
+            const int rr = (half * 8 + it) * RPI + lane / LPR;
             const int row = m0 + wm * 128 + q * 32 + rr;
             if (row < a.M && col < a.N) {
-                const float4 v = *reinterpret_cast<const float4*>(ep + rr * EPL + c);
+                const float4 v = *reinterpret_cast<const float4*>(ep + rr * EPLD + c);
                 float4 o = old[it];
                 o.x += v.x;
                 o.y += v.y;
@@ -405,19 +434,21 @@ __device__ __forceinline__ void epi_dw_quarter(const GemmArgs& a, const f32x16_t
 // ---------------------------------------------------------------------------
 // Row-grouped GEMM: C[rows, N] = A[rows, K] * B_w[K, N] for every plan group.
 // ---------------------------------------------------------------------------
-template <int MODE, int EPI>
-__global__ __launch_bounds__(256, 1) void gemm_rows_kernel(GemmArgs a) {
+template <int MODE, int EPI, int WN>
+__global__ __launch_bounds__(128 * WN, 1) void gemm_rows_kernel(GemmArgs a) {
+    using L = WL<WN>;
+    constexpr int NTHR = L::NTHR;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     __shared__ int s_pref[MAX_GROUPS + 1];
-    __shared__ int s_part[256];
+    __shared__ int s_part[NTHR];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
     const Group* groups = a.w.groups;
     const int ng = min(max(a.w.hdr[HDR_NGROUPS], 0), min(2 * a.w.E, MAX_GROUPS));
 
     // m-tiles per group -> prefix in LDS (each thread scans a contiguous slice)
     {
-        const int per = (ng + 255) / 256;
+        const int per = (ng + NTHR - 1) / NTHR;
         const int lo = tid * per;
         int sum = 0;
         for (int g = lo; g < lo + per && g < ng; ++g) sum += (group_rows(groups[g], a.w) + BM - 1) / BM;
@@ -425,7 +456,7 @@ __global__ __launch_bounds__(256, 1) void gemm_rows_kernel(GemmArgs a) {
         __syncthreads();
         if (tid == 0) {
             int run = 0;
-            for (int i = 0; i < 256; ++i) {
+            for (int i = 0; i < NTHR; ++i) {
                 const int v = s_part[i];
                 s_part[i] = run;
                 run += v;
@@ -437,7 +468,7 @@ __global__ __launch_bounds__(256, 1) void gemm_rows_kernel(GemmArgs a) {
             s_pref[g] = run;
             run += (group_rows(groups[g], a.w) + BM - 1) / BM;
         }
-        if (tid == 255) s_pref[ng] = run;
+        if (tid == NTHR - 1) s_pref[ng] = run;
         __syncthreads();
     }
     const int NT = a.ntiles_n;
@@ -446,9 +477,9 @@ __global__ __launch_bounds__(256, 1) void gemm_rows_kernel(GemmArgs a) {
     const int xcd = blockIdx.x % nxcd, li = blockIdx.x / nxcd, per_wg = gridDim.x / nxcd;
     const int chunk = (total + nxcd - 1) / nxcd;
     const int t_lo = xcd * chunk, t_hi = min(total, t_lo + chunk);
-    float* ep = reinterpret_cast<float*>(smem) + wave * 32 * EPL;
+    float* ep = reinterpret_cast<float*>(smem) + wave * 32 * L::EPL;
     const int nst = a.K / BK;
-    const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds_addr(smem) + wave * 4 * 1024);
+    const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds_addr(smem) + wave * L::PARTS * 1024);
 
     for (int t = t_lo + li; t < t_hi; t += per_wg) {
         int lo = 0, hi = ng - 1;
@@ -466,14 +497,13 @@ __global__ __launch_bounds__(256, 1) void gemm_rows_kernel(GemmArgs a) {
         const uint16_t* W = gr.wsel >= 0 ? a.Bhome + (size_t)gr.wsel * a.bstride
                                          : a.Bslot + (size_t)(-1 - gr.wsel) * a.bstride;
 
-        // per-lane sources of the 4 DMA loads per operand and step
-        const uint16_t* ap[4];
-        const uint16_t* bp[4];
-        bool bmove[4];
-        long long bstep;
+        // per-lane sources of this wave's DMA loads (PARTS per operand and step)
+        const uint16_t* ap[L::PARTS];
+        const uint16_t* bp[L::PARTS];
+        bool bmove[L::PARTS];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int p = (wave * 4 + i) * 64 + lane;
+        for (int i = 0; i < L::PARTS; ++i) {
+            const int p = (wave * L::PARTS + i) * 64 + lane;
             {   // A: k-contiguous activations, rows beyond the group clamp to its last row
                 const int r = p >> 2, c = (p & 3) ^ ((r >> 2) & 3);
                 ap[i] = a.A + (size_t)(row0 + min(r, mvalid - 1)) * a.lda + c * 8;
@@ -497,42 +527,44 @@ __global__ __launch_bounds__(256, 1) void gemm_rows_kernel(GemmArgs a) {
                 bp[i] = bmove[i] ? W + (size_t)k * a.ldb + col : a.w.zeros + c * 8;
             }
         }
-        bstep = MODE == ROWS_BK ? (long long)BK : (long long)BK * a.ldb;
+        const long long bstep = MODE == ROWS_BK ? (long long)BK : (long long)BK * a.ldb;
 
-        f32x16_t acc[4][4];
-        zero_acc(acc);
-        pipeline<true, MODE == ROWS_BK, EPI>(acc, smem, nst, wm, wn, lane, [&](int s, int buf, int i) {
+        f32x16_t acc[4][L::TN];
+        zero_acc<L::TN>(acc);
+        pipeline<true, MODE == ROWS_BK, EPI, WN>(acc, smem, nst, wm, wn, lane, [&](int s, int buf, int i) {
             const uint32_t l = lds_wave + buf * STAGE_BYTES + i * 1024;
             dma16(ap[i] + (size_t)s * BK, l);
             dma16(bmove[i] ? bp[i] + (size_t)s * bstep : bp[i], l + OP_BYTES);
         });
-        epi_rows_quarter<EPI, 0>(a, acc, ep, wm, wn, lane, nt, row0, mvalid);
-        epi_rows_quarter<EPI, 1>(a, acc, ep, wm, wn, lane, nt, row0, mvalid);
-        epi_rows_quarter<EPI, 2>(a, acc, ep, wm, wn, lane, nt, row0, mvalid);
-        epi_rows_quarter<EPI, 3>(a, acc, ep, wm, wn, lane, nt, row0, mvalid);
+        epi_rows_quarter<EPI, WN, 0>(a, acc, ep, wm, wn, lane, nt, row0, mvalid);
+        epi_rows_quarter<EPI, WN, 1>(a, acc, ep, wm, wn, lane, nt, row0, mvalid);
+        epi_rows_quarter<EPI, WN, 2>(a, acc, ep, wm, wn, lane, nt, row0, mvalid);
+        epi_rows_quarter<EPI, WN, 3>(a, acc, ep, wm, wn, lane, nt, row0, mvalid);
         block_sync();   // the ring is reused by the next tile's loads
     }
 }
 
 // ---------------------------------------------------------------------------
-// Weight-gradient GEMM: dW[M, N] += A^T B over the target's row segments, where A = [rows, M]
-// and B = [rows, N] are read m/n-contiguous.  Targets: t < E is home expert t (its home rows
-// plus its fallback replicas, in plan order), t >= E is prefetch slot t - E.
+// Weight-gradient GEMM: dW[M, N] = A^T B (or += with MOONEP_GRAD_ACCUM) over the target's row
+// segments, where A = [rows, M] and B = [rows, N] are read m/n-contiguous.  Targets: t < E is
+// home expert t (its home rows plus its fallback replicas, in plan order), t >= E is prefetch
+// slot t - E.  Tiles are handed out dynamically, targets in descending row order.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256, 1) void gemm_dw_kernel(GemmArgs a) {
+template <int WN>
+__global__ __launch_bounds__(128 * WN, 1) void gemm_dw_kernel(GemmArgs a) {
+    using L = WL<WN>;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     __shared__ Segment s_seg[kMaxR + 1];
     __shared__ int s_tile[2];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
     const PlanWs& w = a.w;
     const int MT = (a.M + BM - 1) / BM, NT = a.ntiles_n;
     const int per_target = MT * NT;
     const int total = (w.E + w.R * w.B) * per_target;
-    float* ep = reinterpret_cast<float*>(smem) + wave * 32 * EPL;
-    const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds_addr(smem) + wave * 4 * 1024);
+    float* ep = reinterpret_cast<float*>(smem) + wave * 32 * L::EPL;
+    const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds_addr(smem) + wave * L::PARTS * 1024);
 
-    // tiles are handed out dynamically, targets in descending row order (largest first)
     for (int iter = 0;; ++iter) {
         if (tid == 0) s_tile[iter & 1] = atomicAdd(a.counter, 1);
         wait_lgkm0();
@@ -569,14 +601,14 @@ __global__ __launch_bounds__(256, 1) void gemm_dw_kernel(GemmArgs a) {
         int nst = 0;
         for (int i = 0; i < nseg; ++i) nst += (s_seg[i].rows + BK - 1) / BK;
         const int m0 = mt * BM, n0 = nt * BN;
-        f32x16_t acc[4][4];
-        zero_acc(acc);
+        f32x16_t acc[4][L::TN];
+        zero_acc<L::TN>(acc);
         if (nst > 0) {
-            int kk_i[4], ac[4], bc[4], zc[4];
-            bool aok[4], bok[4];
+            int kk_i[L::PARTS], ac[L::PARTS], bc[L::PARTS], zc[L::PARTS];
+            bool aok[L::PARTS], bok[L::PARTS];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int p = (wave * 4 + i) * 64 + lane;
+            for (int i = 0; i < L::PARTS; ++i) {
+                const int p = (wave * L::PARTS + i) * 64 + lane;
                 const int k = p >> 5, c = (p & 31) ^ ((k & 3) << 2);
                 kk_i[i] = k;
                 zc[i] = c * 8;
@@ -588,14 +620,14 @@ __global__ __launch_bounds__(256, 1) void gemm_dw_kernel(GemmArgs a) {
             // issue cursor over the segments (runs NSTAGE-1 steps ahead of the compute)
             int iseg = 0, ikoff = 0;
             Segment icur = s_seg[0];
-            pipeline<false, false, EPI_ACC_F32>(acc, smem, nst, wm, wn, lane, [&](int, int buf, int i) {
+            pipeline<false, false, EPI_ACC_F32, WN>(acc, smem, nst, wm, wn, lane, [&](int, int buf, int i) {
                 const uint32_t l = lds_wave + buf * STAGE_BYTES + i * 1024;
                 const int kr = ikoff + kk_i[i];
                 const bool v = kr < icur.rows;
                 const size_t row = (size_t)(icur.row0 + kr);
                 dma16(v && aok[i] ? a.A + row * a.lda + ac[i] : w.zeros + zc[i], l);
                 dma16(v && bok[i] ? a.B + row * a.ldb + bc[i] : w.zeros + zc[i], l + OP_BYTES);
-                if (i == 3) {    // step issued: advance the cursor
+                if (i == L::PARTS - 1) {    // step issued: advance the cursor
                     ikoff += BK;
                     if (ikoff >= icur.rows) {
                         ikoff = 0;
@@ -608,10 +640,10 @@ __global__ __launch_bounds__(256, 1) void gemm_dw_kernel(GemmArgs a) {
             continue;           // nothing to add
         }
         // (an expert without rows gets a zero gradient when the outputs are written)
-        epi_dw_quarter<0>(a, acc, ep, wm, wn, lane, out, m0, n0);
-        epi_dw_quarter<1>(a, acc, ep, wm, wn, lane, out, m0, n0);
-        epi_dw_quarter<2>(a, acc, ep, wm, wn, lane, out, m0, n0);
-        epi_dw_quarter<3>(a, acc, ep, wm, wn, lane, out, m0, n0);
+        epi_dw_quarter<WN, 0>(a, acc, ep, wm, wn, lane, out, m0, n0);
+        epi_dw_quarter<WN, 1>(a, acc, ep, wm, wn, lane, out, m0, n0);
+        epi_dw_quarter<WN, 2>(a, acc, ep, wm, wn, lane, out, m0, n0);
+        epi_dw_quarter<WN, 3>(a, acc, ep, wm, wn, lane, out, m0, n0);
         block_sync();
     }
 }
@@ -638,13 +670,22 @@ static bool set_smem(K kernel) {
                                hipFuncAttributeMaxDynamicSharedMemorySize, GEMM_SMEM) == hipSuccess;
 }
 
+// waves along N of each kernel (2: 4 waves of 128x128; 4: 8 waves of 128x64)
+#ifndef MOONEP_WN_ROWS
+#define MOONEP_WN_ROWS 4
+#endif
+#ifndef MOONEP_WN_DW
+#define MOONEP_WN_DW 4
+#endif
+
 static int launch_rows(int epi, int mode, const GemmArgs& a, hipStream_t s) {
     const int grid = (num_cus() / 8) * 8;
-#define MOONEP_ROWS(M_, E_)                                                                    \
-    do {                                                                                       \
-        static bool ok = set_smem(gemm_rows_kernel<M_, E_>);                                   \
-        if (!ok) return MOONEP_EHIP;                                                           \
-        hipLaunchKernelGGL((gemm_rows_kernel<M_, E_>), dim3(grid), dim3(256), GEMM_SMEM, s, a); \
+    constexpr int WN = MOONEP_WN_ROWS;
+#define MOONEP_ROWS(M_, E_)                                                                            \
+    do {                                                                                               \
+        static bool ok = set_smem(gemm_rows_kernel<M_, E_, WN>);                                       \
+        if (!ok) return MOONEP_EHIP;                                                                   \
+        hipLaunchKernelGGL((gemm_rows_kernel<M_, E_, WN>), dim3(grid), dim3(128 * WN), GEMM_SMEM, s, a); \
     } while (0)
     if (epi == EPI_SWIGLU_FWD && mode == ROWS_BN) MOONEP_ROWS(ROWS_BN, EPI_SWIGLU_FWD);
     else if (epi == EPI_STORE && mode == ROWS_BN) MOONEP_ROWS(ROWS_BN, EPI_STORE);
@@ -657,10 +698,11 @@ static int launch_rows(int epi, int mode, const GemmArgs& a, hipStream_t s) {
 }
 
 static int launch_dw(const GemmArgs& a, hipStream_t s) {
-    static bool ok = set_smem(gemm_dw_kernel);
+    constexpr int WN = MOONEP_WN_DW;
+    static bool ok = set_smem(gemm_dw_kernel<WN>);
     if (!ok) return MOONEP_EHIP;
     const int grid = (num_cus() / 8) * 8;
-    hipLaunchKernelGGL(gemm_dw_kernel, dim3(grid), dim3(256), GEMM_SMEM, s, a);
+    hipLaunchKernelGGL(gemm_dw_kernel<WN>, dim3(grid), dim3(128 * WN), GEMM_SMEM, s, a);
     MOONEP_LAUNCH_CHECK();
     return MOONEP_OK;
 }
