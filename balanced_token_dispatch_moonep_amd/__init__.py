@@ -17,6 +17,7 @@ from typing import Optional
 
 __all__ = [
     "MoonEPError", "Dims", "LIB_PATH", "lib", "NSTATS", "STAT_NAMES", "TRAINING", "F32_ROWS", "GRAD_ACCUM",
+    "PHASE_GATE_UP", "PHASE_DOWN", "PHASE_DACT", "PHASE_DX", "PHASE_DW2", "PHASE_DW13",
     "ST_BAD_ID", "ST_DUP_ID", "ST_CAPACITY", "ST_OVERFLOW", "ST_TRAIN_FALLBACK",
     "moonep_plan_workspace_bytes", "moonep_plan", "moonep_prefetch", "moonep_dispatch",
     "moonep_combine", "moonep_grouped_ffn", "moonep_grouped_ffn_backward", "moonep_reduce_grad",
@@ -28,6 +29,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoonep.s
 TRAINING = 1
 F32_ROWS = 2
 GRAD_ACCUM = 4
+# phase selection of the expert FFN calls (one GEMM kernel each; none set = all of the call's)
+PHASE_GATE_UP, PHASE_DOWN = 8, 16
+PHASE_DACT, PHASE_DX, PHASE_DW2, PHASE_DW13 = 32, 64, 128, 256
 NSTATS = 16
 ST_BAD_ID, ST_DUP_ID, ST_CAPACITY, ST_OVERFLOW, ST_TRAIN_FALLBACK = 1, 2, 4, 8, 16
 STAT_NAMES = (
@@ -56,9 +60,13 @@ class Dims(ctypes.Structure):
                 ("I", ctypes.c_int32), ("flags", ctypes.c_uint32)]
 
     @classmethod
-    def make(cls, R, E, B, S, K, H, I=0, training=False, f32_rows=False, grad_accum=False) -> "Dims":
+    def make(cls, R, E, B, S, K, H, I=0, training=False, f32_rows=False, grad_accum=False, phases=0) -> "Dims":
         flags = (TRAINING if training else 0) | (F32_ROWS if f32_rows else 0) | (GRAD_ACCUM if grad_accum else 0)
+        flags |= int(phases)
         return cls(R, E, B, S, K, H, I, flags)
+
+    def with_flags(self, flags: int) -> "Dims":
+        return Dims(self.R, self.E, self.B, self.S, self.K, self.H, self.I, int(flags))
 
     @property
     def C(self) -> int:

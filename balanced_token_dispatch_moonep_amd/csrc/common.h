@@ -17,6 +17,9 @@ constexpr int kMaxG = 64;            // home experts per rank
 constexpr int kMaxB = 64;
 constexpr int kMaxK = 16;
 constexpr int kZeroElems = 512;      // zero bf16 elements kept in the plan workspace
+constexpr uint32_t kFwdPhases = MOONEP_PHASE_GATE_UP | MOONEP_PHASE_DOWN;
+constexpr uint32_t kBwdPhases = MOONEP_PHASE_DACT | MOONEP_PHASE_DX | MOONEP_PHASE_DW2 | MOONEP_PHASE_DW13;
+constexpr uint32_t kPhaseBits = kFwdPhases | kBwdPhases;
 
 // Header words of the plan workspace.
 enum HdrWord {
@@ -121,7 +124,7 @@ inline int check_dims(const moonep_dims_t* d, bool need_ffn) {
     if (d->S < 1 || d->K < 1 || d->K > kMaxK || d->K > d->E) return MOONEP_EINVAL;
     if ((int64_t)d->R * d->S * d->K > (int64_t)1 << 30) return MOONEP_EINVAL;
     if (d->H < 8 || d->H % 8 != 0) return MOONEP_EINVAL;
-    if (d->flags & ~(MOONEP_TRAINING | MOONEP_F32_ROWS | MOONEP_GRAD_ACCUM)) return MOONEP_EINVAL;
+    if (d->flags & ~(MOONEP_TRAINING | MOONEP_F32_ROWS | MOONEP_GRAD_ACCUM | kPhaseBits)) return MOONEP_EINVAL;
     if (need_ffn && (d->I < 8 || d->I % 8 != 0)) return MOONEP_EINVAL;
     return MOONEP_OK;
 }

@@ -550,7 +550,8 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_rows_kernel(GemmArgs a) {
 // home expert t (its home rows plus its fallback replicas, in plan order), t >= E is prefetch
 // slot t - E.  Tiles are handed out dynamically, targets in descending row order.
 // ---------------------------------------------------------------------------
-template <int WN>
+// WHICH (2 or 13) only separates the two weight-gradient launches' kernel names in traces.
+template <int WN, int WHICH>
 __global__ __launch_bounds__(128 * WN, 1) void gemm_dw_kernel(GemmArgs a) {
     using L = WL<WN>;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -697,14 +698,24 @@ static int launch_rows(int epi, int mode, const GemmArgs& a, hipStream_t s) {
     return MOONEP_OK;
 }
 
+// Resets the launch's tile counter, then runs the dynamic-tile weight-gradient kernel.
+template <int WHICH>
 static int launch_dw(const GemmArgs& a, hipStream_t s) {
     constexpr int WN = MOONEP_WN_DW;
-    static bool ok = set_smem(gemm_dw_kernel<WN>);
+    static bool ok = set_smem(gemm_dw_kernel<WN, WHICH>);
     if (!ok) return MOONEP_EHIP;
+    hipLaunchKernelGGL(reset_counters_kernel, dim3(1), dim3(64), 0, s, a.counter, 1);
+    MOONEP_LAUNCH_CHECK();
     const int grid = (num_cus() / 8) * 8;
-    hipLaunchKernelGGL(gemm_dw_kernel<WN>, dim3(grid), dim3(128 * WN), GEMM_SMEM, s, a);
+    hipLaunchKernelGGL((gemm_dw_kernel<WN, WHICH>), dim3(grid), dim3(128 * WN), GEMM_SMEM, s, a);
     MOONEP_LAUNCH_CHECK();
     return MOONEP_OK;
+}
+
+// Phases of one call selected by flags: the call's bits that are set, or all of them.
+static uint32_t phases(const moonep_dims_t* d, uint32_t mine) {
+    const uint32_t p = d->flags & mine;
+    return p ? p : mine;
 }
 
 static int check_ffn_dims(const moonep_dims_t* d) {
@@ -755,8 +766,12 @@ extern "C" int moonep_grouped_ffn(const moonep_dims_t* dims, const void* plan_ws
     a.ldo = I;
     a.gu = static_cast<uint16_t*>(gu_save);
     a.ntiles_n = (I + 127) / 128;
-    rc = launch_rows(EPI_SWIGLU_FWD, ROWS_BN, a, s);
-    if (rc != MOONEP_OK) return rc;
+    const uint32_t ph = phases(dims, kFwdPhases);
+    if (ph & MOONEP_PHASE_GATE_UP) {
+        rc = launch_rows(EPI_SWIGLU_FWD, ROWS_BN, a, s);
+        if (rc != MOONEP_OK) return rc;
+    }
+    if (!(ph & MOONEP_PHASE_DOWN)) return MOONEP_OK;
     // y = act W2
     a.A = static_cast<const uint16_t*>(act);
     a.lda = I;
@@ -803,9 +818,7 @@ extern "C" int moonep_grouped_ffn_backward(const moonep_dims_t* dims, const void
     GemmArgs a{};
     plan_ws_layout(dims, const_cast<void*>(plan_ws), &a.w);
     uint16_t* gu = static_cast<uint16_t*>(const_cast<void*>(gu_save));
-    // tile counters of the two weight-gradient launches
-    hipLaunchKernelGGL(reset_counters_kernel, dim3(1), dim3(64), 0, s, a.w.counters, 2);
-    MOONEP_LAUNCH_CHECK();
+    const uint32_t ph = phases(dims, kBwdPhases);
     // dA = dY W2^T (B = W2 [I, H] is k-contiguous), fused SwiGLU' written over Gt|U
     a.A = static_cast<const uint16_t*>(dy);
     a.lda = H;
@@ -818,8 +831,10 @@ extern "C" int moonep_grouped_ffn_backward(const moonep_dims_t* dims, const void
     a.I = I;
     a.gu = gu;
     a.ntiles_n = (I + BN - 1) / BN;
-    rc = launch_rows(EPI_SWIGLU_BWD, ROWS_BK, a, s);
-    if (rc != MOONEP_OK) return rc;
+    if (ph & MOONEP_PHASE_DACT) {
+        rc = launch_rows(EPI_SWIGLU_BWD, ROWS_BK, a, s);
+        if (rc != MOONEP_OK) return rc;
+    }
     // dX = [dGt dU] W13^T (B = W13 [H, 2I] is k-contiguous)
     a.A = gu;
     a.lda = 2 * I;
@@ -833,8 +848,10 @@ extern "C" int moonep_grouped_ffn_backward(const moonep_dims_t* dims, const void
     a.ldo = H;
     a.gu = nullptr;
     a.ntiles_n = (H + BN - 1) / BN;
-    rc = launch_rows(EPI_STORE, ROWS_BK, a, s);
-    if (rc != MOONEP_OK) return rc;
+    if (ph & MOONEP_PHASE_DX) {
+        rc = launch_rows(EPI_STORE, ROWS_BK, a, s);
+        if (rc != MOONEP_OK) return rc;
+    }
     // dW2 = A^T dY  ([I, H])
     GemmArgs d{};
     d.w = a.w;
@@ -849,8 +866,10 @@ extern "C" int moonep_grouped_ffn_backward(const moonep_dims_t* dims, const void
     d.ntiles_n = (H + BN - 1) / BN;
     d.counter = a.w.counters;
     d.accum = (dims->flags & MOONEP_GRAD_ACCUM) ? 1 : 0;
-    rc = launch_dw(d, s);
-    if (rc != MOONEP_OK) return rc;
+    if (ph & MOONEP_PHASE_DW2) {
+        rc = launch_dw<2>(d, s);
+        if (rc != MOONEP_OK) return rc;
+    }
     // dW13 = X^T [dGt dU]  ([H, 2I])
     d.A = static_cast<const uint16_t*>(recv);
     d.lda = H;
@@ -862,5 +881,5 @@ extern "C" int moonep_grouped_ffn_backward(const moonep_dims_t* dims, const void
     d.dw_slot = dw13_red;
     d.ntiles_n = (2 * I + BN - 1) / BN;
     d.counter = a.w.counters + 1;
-    return launch_dw(d, s);
+    return (ph & MOONEP_PHASE_DW13) ? launch_dw<13>(d, s) : MOONEP_OK;
 }

@@ -91,7 +91,8 @@ class MoonEPLayer:
         return self.out
 
     def backward(self, dout, gates):
-        """Gradient of forward(): returns dx [R, S, H]; accumulates dw13 / dw2 (fp32).
+        """Gradient of forward(): returns dx [R, S, H]; writes dw13 / dw2 (fp32; added to them
+        with MOONEP_GRAD_ACCUM), slot replicas' gradients reduced into their home experts.
 
         The saved gate|up activations are overwritten by their gradients."""
         assert self.training and self.d.I > 0

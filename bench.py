@@ -27,6 +27,34 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 
 
+SWEEP = (0.0, 0.5, 2.0, 4.0, 8.0)
+
+# timed call -> the one kernel it launches (name as in rocprofv3 kernel traces); the plan call
+# launches four small kernels and has no entry.  The weight-gradient calls also launch a
+# one-wave counter reset before their GEMM.
+KERNEL_NAMES = {
+    "prefetch": "moonep::prefetch_kernel",
+    "dispatch": "moonep::dispatch_kernel<false, false, 4>",
+    "gemm_gate_up": "moonep::gemm_rows_kernel<0, 0, 4>",
+    "gemm_down": "moonep::gemm_rows_kernel<0, 1, 4>",
+    "combine": "moonep::combine_kernel<false, true, 8, 2>",
+    "dispatch_bwd": "moonep::dispatch_kernel<false, true, 4>",
+    "gemm_dact": "moonep::gemm_rows_kernel<1, 2, 4>",
+    "gemm_dx": "moonep::gemm_rows_kernel<1, 1, 4>",
+    "gemm_dw2": "moonep::gemm_dw_kernel<4, 2>",
+    "gemm_dw13": "moonep::gemm_dw_kernel<4, 13>",
+    "combine_bwd": "moonep::combine_kernel<false, false, 8, 2>",
+    "reduce_grad": "moonep::reduce_grad_kernel",
+}
+# sources each kernel is compiled from (a change to any of them voids its stored counters)
+KERNEL_SOURCES = {
+    "prefetch": ("weights.hip",), "reduce_grad": ("weights.hip",),
+    "dispatch": ("permute.hip",), "combine": ("permute.hip",),
+    "dispatch_bwd": ("permute.hip",), "combine_bwd": ("permute.hip",),
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -35,7 +63,14 @@ def parse():
     p.add_argument("--maxvio", type=float, default=4.0)
     p.add_argument("--no-sweep", action="store_true", help="skip the maxvio sweep")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    p.add_argument("--cpu-tokens", type=int, default=512, help="tokens per rank in the CPU sample")
+    p.add_argument("--cpu-tokens", type=int, default=4096, help="tokens per rank in the CPU sample")
+    p.add_argument("--cpu-groups", type=int, default=8, help="expert groups in the CPU FFN sample")
+    p.add_argument("--traffic-from", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "BENCH_JSON"),
+                   help="no GPU work: reduce two rocprofv3 --pmc runs of this bench (FETCH_SIZE, then "
+                        "WRITE_SIZE) and that run's JSON line to per-launch HBM bytes; writes "
+                        "profiles/hbm_traffic.json and prints a markdown summary")
+    p.add_argument("--stats-from", metavar="DIR",
+                   help="no GPU work: print a markdown table of a rocprofv3 --stats kernel summary")
     return p.parse_args()
 
 
@@ -63,6 +98,13 @@ class Timer:
 
 def main():
     args = parse()
+    if args.traffic_from:
+        return write_traffic(*args.traffic_from)
+    if args.stats_from:
+        return print_stats(args.stats_from)
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the R expert-parallel ranks are emulated as "
               f"partitions of a single MI355X, so --gpus {args.gpus} is not supported.", file=sys.stderr)
@@ -79,7 +121,6 @@ def main():
     torch.cuda.set_device(dev)
     cfg = W.CONFIGS["train"].with_(maxvio=args.maxvio)
     R, E, B, S, K, H, I = cfg.R, cfg.E, cfg.B, cfg.S, cfg.K, cfg.H, cfg.I
-    Mrows = R * S * K
 
     def log(*a):
         print(*a, file=sys.stderr, flush=True)
@@ -101,129 +142,112 @@ def main():
     log("[bench] inputs resident; warming up")
 
     T = Timer(torch)
+    bwd_args = lambda: (L.ws, L.cu, L.recv, L.gu, L.act, L.dy, L.w13, L.w2, L.w13_slot, L.w2_slot, L.drecv,
+                        L.dw13, L.dw2, L.dw13_red, L.dw2_red)
+    dph = {ph: d.with_flags(d.flags | ph) for ph in (M.PHASE_GATE_UP, M.PHASE_DOWN, M.PHASE_DACT, M.PHASE_DX,
+                                                   M.PHASE_DW2, M.PHASE_DW13)}
 
-    def step():
-        T.run("plan", lambda: L.plan(tk))
+    def ffn_fwd_phase(ph):
+        M.moonep_grouped_ffn(dph[ph], L.ws, L.cu, L.recv, L.w13, L.w2, L.w13_slot, L.w2_slot, L.gu, L.act, L.y)
+
+    def ffn_bwd_phase(ph):
+        M.moonep_grouped_ffn_backward(dph[ph], *bwd_args())
+
+    def step(T, gates, tkd, backward=True):
+        # every GEMM phase is its own call, so each kernel is timed on its own
+        T.run("plan", lambda: L.plan(tkd))
         T.run("prefetch", L.prefetch)
         T.run("dispatch", lambda: L.dispatch(x))
-        T.run("ffn_fwd", L.expert_ffn)
-        T.run("combine", lambda: L.combine(g))
-        T.run("dispatch_bwd", lambda: M.moonep_dispatch(d, L.dest, dout, g, L.dy))
-        T.run("ffn_bwd", lambda: M.moonep_grouped_ffn_backward(
-            d, L.ws, L.cu, L.recv, L.gu, L.act, L.dy, L.w13, L.w2, L.w13_slot, L.w2_slot, L.drecv,
-            L.dw13, L.dw2, L.dw13_red, L.dw2_red))
+        T.run("gemm_gate_up", lambda: ffn_fwd_phase(M.PHASE_GATE_UP))
+        T.run("gemm_down", lambda: ffn_fwd_phase(M.PHASE_DOWN))
+        T.run("combine", lambda: L.combine(gates))
+        if not backward:
+            return
+        T.run("dispatch_bwd", lambda: M.moonep_dispatch(d, L.dest, dout, gates, L.dy))
+        T.run("gemm_dact", lambda: ffn_bwd_phase(M.PHASE_DACT))
+        T.run("gemm_dx", lambda: ffn_bwd_phase(M.PHASE_DX))
+        T.run("gemm_dw2", lambda: ffn_bwd_phase(M.PHASE_DW2))
+        T.run("gemm_dw13", lambda: ffn_bwd_phase(M.PHASE_DW13))
         T.run("combine_bwd", lambda: M.moonep_combine(d, L.dest, L.drecv, None, L.dx))
         T.run("reduce_grad", lambda: M.moonep_reduce_grad(d, L.ws, L.dw13, L.dw2, L.dw13_red, L.dw2_red))
 
     for _ in range(args.warmup):
-        step()
+        step(T, g, tk)
     torch.cuda.synchronize()
-    st = L.stats.cpu().numpy()
     T.clear()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        step(T, g, tk)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = T.avg_ms()
+    st = L.stats.cpu().numpy()
     ms_step = wall * 1e3 / args.steps
     log("[bench] per-call ms:", {k: round(v, 4) for k, v in ms.items()}, "step ms", round(ms_step, 3))
 
-    # algorithmic work per call (what the method must move or compute)
-    xbytes = R * S * H * 2
-    rbytes = Mrows * H * 2
-    NW = 3 * H * I
-    n_slot = int(st[2])
-    work = {
-        "plan": ("hbm", 8.0 * Mrows),
-        "prefetch": ("hbm", 2.0 * n_slot * NW * 2),
-        "dispatch": ("hbm", xbytes + rbytes + 4.0 * Mrows),
-        "combine": ("hbm", rbytes + 8.0 * Mrows + xbytes),
-        "dispatch_bwd": ("hbm", xbytes + rbytes + 8.0 * Mrows),
-        "combine_bwd": ("hbm", rbytes + 4.0 * Mrows + xbytes),
-        "ffn_fwd": ("mfma", 6.0 * Mrows * H * I),
-        "ffn_bwd": ("mfma", 12.0 * Mrows * H * I),
-    }
-    # reduce_grad: (8 + 8n) * NW bytes for every expert with n slot replicas; the slot
-    # replicas per expert are read off the device plan (slot rows of cu_seqlens, and the
-    # expert of their first row via dest).
-    cu = L.cu.cpu().numpy()
-    dst = L.dest.cpu().numpy().ravel()
-    tkf = topk.ravel()
-    row_expert = np.full(Mrows, -1, dtype=np.int64)
-    row_expert[dst] = tkf
-    reps = {}
-    for q in range(R):
-        for j in range(B):
-            lo, hi = cu[q, E + j], cu[q, E + j + 1]
-            if hi > lo:
-                e = int(row_expert[q * S * K + lo])
-                reps[e] = reps.get(e, 0) + 1
-    work["reduce_grad"] = ("hbm", float(sum((8 + 8 * n) * NW for n in reps.values())))
-
-    rooflines = {}
-    for k, (bound, amount) in work.items():
-        t = ms.get(k, 0.0) / 1e3
-        if bound == "hbm":
-            ach = amount / t / 1e9 if t > 0 else 0.0
-            rooflines[k] = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                            "frac": round(ach / HBM_PEAK_GBS, 4), "ms": round(ms[k], 4), "bytes": amount}
-        else:
-            ach = amount / t / 1e12 if t > 0 else 0.0
-            rooflines[k] = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
-                            "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
-                            "ms": round(ms[k], 4), "flops": amount}
+    work = algorithmic_work(cfg, st, L.cu.cpu().numpy(), L.dest.cpu().numpy().ravel(), topk)
+    rooflines = {k: roofline_of(k, work[k], ms[k]) for k in ms}
+    fwd_keys, bwd_keys = ("gemm_gate_up", "gemm_down"), ("gemm_dact", "gemm_dx", "gemm_dw2", "gemm_dw13")
     dc_keys = ("dispatch", "combine", "dispatch_bwd", "combine_bwd")
     dc_bytes = sum(work[k][1] for k in dc_keys)
     dc_ms = sum(ms[k] for k in dc_keys)
     value = dc_bytes / (dc_ms / 1e3) / 1e9
-    gemm_tflops = (work["ffn_fwd"][1] + work["ffn_bwd"][1]) / ((ms["ffn_fwd"] + ms["ffn_bwd"]) / 1e3) / 1e12
-    dom = max(ms, key=lambda k: ms[k])
+    gemm_keys = fwd_keys + bwd_keys
+    gemm_tflops = sum(work[k][1] for k in gemm_keys) / (sum(ms[k] for k in gemm_keys) / 1e3) / 1e12
+    fwd_tflops = sum(work[k][1] for k in fwd_keys) / (sum(ms[k] for k in fwd_keys) / 1e3) / 1e12
+    bwd_tflops = sum(work[k][1] for k in bwd_keys) / (sum(ms[k] for k in bwd_keys) / 1e3) / 1e12
+    # dominant kernel: the single-kernel call with the longest average launch
+    dom = max((k for k in ms if k in KERNEL_NAMES), key=lambda k: ms[k])
     r = rooflines[dom]
     roofline = {"bound": r["bound"], "achieved": r["achieved"], "peak": r["peak"], "unit": r["unit"],
-                "frac": r["frac"], "traffic": None, "kernel": f"moonep_{dom}" if not dom.endswith("_bwd")
-                else "moonep_grouped_ffn_backward" if dom == "ffn_bwd" else f"moonep_{dom}"}
+                "frac": r["frac"], "traffic": traffic_of(dom, work[dom][2]), "kernel": KERNEL_NAMES[dom],
+                "call": dom, "ms": r["ms"], "per_launch": work[dom][3]}
 
-    # ---- maxvio sweep (same shapes): plan, dispatch+combine, GEMM forward -------------------
+    # ---- maxvio sweep (same shapes): the whole training step per maxvio ----------------------
     sweep = []
     if not args.no_sweep:
-        for mv in (0.0, 0.5, 2.0, 4.0, 8.0):
+        for mv in SWEEP:
             c2 = cfg.with_(maxvio=mv)
             tk2, g2, lam2 = W.routing_for(c2)
             tkd, gd = torch.from_numpy(tk2).to(dev), torch.from_numpy(g2).to(dev)
             T2 = Timer(torch)
-            for it in range(4):
-                T2.run("plan", lambda: L.plan(tkd))
-                T2.run("prefetch", L.prefetch)
-                T2.run("dispatch", lambda: L.dispatch(x))
-                T2.run("ffn_fwd", L.expert_ffn)
-                T2.run("combine", lambda: L.combine(gd))
-                if it == 0:
-                    torch.cuda.synchronize()
-                    T2.clear()
+            step(T2, gd, tkd)
+            torch.cuda.synchronize()
+            T2.clear()
+            for it in range(3):
+                step(T2, gd, tkd)
             torch.cuda.synchronize()
             m2 = T2.avg_ms()
             s2 = L.stats.cpu().numpy()
-            Lx = np.bincount(tk2.ravel(), minlength=E).astype(np.float64)
-            sweep.append({
-                "maxvio": round(float((Lx.max() - Lx.mean()) / Lx.mean()), 3), "lambda": round(lam2, 4),
-                "replicas": int(s2[1]), "fallback_replicas": int(s2[3]),
-                "migrated_frac": round(int(s2[5]) / Mrows, 4),
-                "rank_peak_over_mean": round(int(s2[8]) / (S * K), 4),
-                "plan_us": round(m2["plan"] * 1e3, 1), "prefetch_ms": round(m2["prefetch"], 4),
-                "dispatch_ms": round(m2["dispatch"], 4), "combine_ms": round(m2["combine"], 4),
-                "dc_GBps": round((work["dispatch"][1] + work["combine"][1]) /
-                                 ((m2["dispatch"] + m2["combine"]) / 1e3) / 1e9, 1),
-                "gemm_fwd_ms": round(m2["ffn_fwd"], 3),
-                "gemm_fwd_TFLOPs": round(work["ffn_fwd"][1] / (m2["ffn_fwd"] / 1e3) / 1e12, 1),
-            })
+            w2k = algorithmic_work(c2, s2, L.cu.cpu().numpy(), L.dest.cpu().numpy().ravel(), tk2)
+            sweep.append(sweep_entry(c2, tk2, lam2, s2, m2, w2k, "train"))
             log("[bench] sweep", sweep[-1])
+        # inference variant: B = 3 prefetch slots, fallback replicas read their home rows
+        ci = cfg.with_(B=3)
+        di = M.Dims.make(R, E, 3, S, K, H, I, training=False)
+        Li = MoonEPLayer(di, w13=w13, w2=w2, training=False)
+        Ti = Timer(torch)
+        for it in range(4):
+            Ti.run("plan", lambda: Li.plan(tk))
+            Ti.run("prefetch", Li.prefetch)
+            Ti.run("dispatch", lambda: Li.dispatch(x))
+            Ti.run("ffn_fwd", Li.expert_ffn)
+            Ti.run("combine", lambda: Li.combine(g))
+            if it == 0:
+                torch.cuda.synchronize()
+                Ti.clear()
+        torch.cuda.synchronize()
+        si = Li.stats.cpu().numpy()
+        wi = algorithmic_work(ci, si, Li.cu.cpu().numpy(), Li.dest.cpu().numpy().ravel(), topk)
+        sweep.append(sweep_entry(ci, topk, lam, si, Ti.avg_ms(), wi, "inference_B3"))
+        log("[bench] sweep", sweep[-1])
+        del Li
 
     # ---- CPU oracle baseline on a bounded sample of the same workload ----------------------
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(cfg, args.cpu_tokens, log)
+        cpu = cpu_baseline(cfg, args.cpu_tokens, args.cpu_groups, log)
 
     out = {
         "metric": "dispatch+combine GB/s and grouped-GEMM TFLOP/s vs maxvio, % of roofline, 1 GPU",
@@ -246,6 +270,8 @@ def main():
         "dc_frac_hbm": round(value / HBM_PEAK_GBS, 4),
         "gemm_TFLOPs": round(gemm_tflops, 1),
         "gemm_frac_mfma": round(gemm_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "gemm_fwd_TFLOPs": round(fwd_tflops, 1),
+        "gemm_bwd_TFLOPs": round(bwd_tflops, 1),
         "roofline": roofline,
         "rooflines": rooflines,
         "sweep": sweep,
@@ -255,7 +281,225 @@ def main():
     return 0
 
 
-def cpu_baseline(cfg, tokens, log):
+def algorithmic_work(cfg, st, cu, dst, topk):
+    """Per timed call: (bound, algorithmic bytes or flops, algorithmic HBM bytes, per-launch text).
+
+    Bytes count what the method must move (each operand read once, each result written once);
+    flops count real rows only (2 per multiply-add), never padding."""
+    import numpy as np
+    R, E, B, S, K, H, I = cfg.R, cfg.E, cfg.B, cfg.S, cfg.K, cfg.H, cfg.I
+    Mr = R * S * K
+    xbytes, rbytes, NW = R * S * H * 2, Mr * H * 2, 3 * H * I
+    n_slot = int(st[2])
+    # expert of each slot replica (slot rows of cu_seqlens; the expert of their first row via dest)
+    row_expert = np.full(Mr, -1, dtype=np.int64)
+    row_expert[dst] = topk.ravel()
+    reps = {}
+    for q in range(R):
+        for j in range(B):
+            lo, hi = cu[q, E + j], cu[q, E + j + 1]
+            if hi > lo:
+                e = int(row_expert[q * S * K + lo])
+                reps[e] = reps.get(e, 0) + 1
+    rg = float(sum((8 + 8 * n) * NW for n in reps.values()))
+    mhi = float(Mr) * H * I
+    # GEMM operand bytes (each operand and result once): A rows, the weights of every group, out
+    wgroups = E + n_slot + int(st[3])
+    gem = {
+        "gemm_gate_up": (4 * mhi, Mr * H * 2 + wgroups * H * 2 * I * 2 + Mr * I * 2 * 3),
+        "gemm_down": (2 * mhi, Mr * I * 2 + wgroups * I * H * 2 + Mr * H * 2),
+        "gemm_dact": (2 * mhi, Mr * H * 2 + wgroups * I * H * 2 + Mr * 2 * I * 2 * 2),
+        "gemm_dx": (4 * mhi, Mr * 2 * I * 2 + wgroups * H * 2 * I * 2 + Mr * H * 2),
+        "gemm_dw2": (2 * mhi, Mr * I * 2 + Mr * H * 2 + (E + n_slot) * I * H * 4),
+        "gemm_dw13": (4 * mhi, Mr * H * 2 + Mr * 2 * I * 2 + (E + n_slot) * H * 2 * I * 4),
+    }
+    work = {
+        "plan": ("hbm", 8.0 * Mr, 8.0 * Mr, f"topk read + dest write, {Mr} pairs (4 kernels)"),
+        "prefetch": ("hbm", 2.0 * n_slot * NW * 2, 2.0 * n_slot * NW * 2,
+                     f"{n_slot} slot replicas x 2 x {NW} bf16 weights (read + write)"),
+        "dispatch": ("hbm", xbytes + rbytes + 4.0 * Mr, xbytes + rbytes + 4.0 * Mr,
+                     f"{R * S} rows read once, {Mr} rows written, {Mr} dest"),
+        "combine": ("hbm", rbytes + 8.0 * Mr + xbytes, rbytes + 8.0 * Mr + xbytes,
+                    f"{Mr} rows read, {R * S} rows written, dest + gates"),
+        "dispatch_bwd": ("hbm", xbytes + rbytes + 8.0 * Mr, xbytes + rbytes + 8.0 * Mr,
+                         f"{R * S} rows read once, {Mr} scaled rows written, dest + gates"),
+        "combine_bwd": ("hbm", rbytes + 4.0 * Mr + xbytes, rbytes + 4.0 * Mr + xbytes,
+                        f"{Mr} rows read, {R * S} rows written, dest"),
+        "reduce_grad": ("hbm", rg, rg, f"{len(reps)} replicated experts, {sum(reps.values())} slot replicas, "
+                                       f"(8 + 8n) x {NW} bytes each"),
+    }
+    for k, (fl, by) in gem.items():
+        work[k] = ("mfma", fl, float(by), f"{fl / mhi:.0f} x M*H*I flops, M={Mr} real rows, H={H}, I={I}")
+    return work
+
+
+def roofline_of(name, w, ms):
+    bound, amount = w[0], w[1]
+    t = ms / 1e3
+    if bound == "hbm":
+        ach = amount / t / 1e9 if t > 0 else 0.0
+        return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "ms": round(ms, 4), "bytes": amount}
+    ach = amount / t / 1e12 if t > 0 else 0.0
+    return {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "ms": round(ms, 4), "flops": amount,
+            "operand_bytes": w[2]}
+
+
+def _sources_digest(call):
+    import hashlib
+    csrc = os.path.join(ROOT, "balanced_token_dispatch_moonep_amd", "csrc")
+    files = KERNEL_SOURCES.get(call, ("gemm.hip",)) + ("common.h",)
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_of(call, algorithmic_bytes):
+    """HBM bytes per launch of the call's kernel from the stored rocprofv3 FETCH_SIZE / WRITE_SIZE
+    counts (scaled by a copy kernel of known size), or None when none are stored for the kernel
+    as it is now built."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(call)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("sources") != _sources_digest(call):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def _kernel_call(kname):
+    """The timed call whose kernel a rocprofv3 kernel name is, or None."""
+    n = kname[5:] if kname.startswith("void ") else kname
+    for call, k in KERNEL_NAMES.items():
+        if n.startswith(k + "("):
+            return call
+    return None
+
+
+def _pmc_per_dispatch(d, counter):
+    """Mean per dispatch of one counter, per kernel name, from a rocprofv3 -f csv output tree."""
+    import csv
+    import glob
+    tot = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                if row["Counter_Name"] != counter:
+                    continue
+                key = (row["Kernel_Name"], row["Dispatch_Id"])
+                tot[key] = tot.get(key, 0.0) + float(row["Counter_Value"])
+    per = {}
+    for (k, _), v in tot.items():
+        per.setdefault(k, []).append(v)
+    return {k: (sum(v) / len(v), len(v)) for k, v in per.items()}
+
+
+def write_traffic(fetch_dir, write_dir, bench_json):
+    """FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of every timed kernel, scaled by what the same
+    counters read for the weight prefetch, a plain copy of known size."""
+    with open(bench_json) as f:
+        line = [ln for ln in f if ln.startswith("{")][-1]
+    run = json.loads(line)
+    fetch = _pmc_per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = _pmc_per_dispatch(write_dir, "WRITE_SIZE")
+    calls = {}
+    for k in set(fetch) | set(write):
+        c = _kernel_call(k)
+        if c:
+            calls[c] = k
+    if "prefetch" not in calls:
+        print("no prefetch kernel in the counter runs: nothing to calibrate against", file=sys.stderr)
+        return 1
+    copy_bytes = run["rooflines"]["prefetch"]["bytes"] / 2       # read once, written once
+    kf = copy_bytes / (fetch[calls["prefetch"]][0] * 1024.0)
+    kw = copy_bytes / (write[calls["prefetch"]][0] * 1024.0)
+    out = {"_calibration": {"copy_kernel": KERNEL_NAMES["prefetch"], "copy_bytes_each_way": copy_bytes,
+                            "fetch_factor": round(kf, 4), "write_factor": round(kw, 4),
+                            "workload": run["config"]}}
+    rows = []
+    for c in KERNEL_NAMES:
+        if c not in calls:
+            continue
+        k = calls[c]
+        fb = fetch.get(k, (0.0, 0))[0] * 1024.0 * kf
+        wb = write.get(k, (0.0, 0))[0] * 1024.0 * kw
+        r = run["rooflines"].get(c, {})
+        alg = r.get("bytes", r.get("operand_bytes"))
+        out[c] = {"kernel": KERNEL_NAMES[c], "fetch_bytes": round(fb), "write_bytes": round(wb),
+                  "hbm_bytes_per_launch": round(fb + wb), "sources": _sources_digest(c),
+                  "dispatches": fetch.get(k, (0.0, 0))[1]}
+        rows.append(f"| `{KERNEL_NAMES[c]}` | {c} | {fb / 1e9:.3f} | {wb / 1e9:.3f} | {(fb + wb) / 1e9:.3f} | "
+                    + (f"{alg / 1e9:.3f} | {(fb + wb) / alg:.2f} |" if alg else "— | — |"))
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(f"Copy calibration: `{KERNEL_NAMES['prefetch']}` moves {copy_bytes / 1e9:.3f} GB each way; "
+          f"FETCH_SIZE x {kf:.4f}, WRITE_SIZE x {kw:.4f}.\n")
+    print("| kernel | call | fetch GB | write GB | HBM GB / launch | algorithmic GB | ratio |")
+    print("|---|---|---:|---:|---:|---:|---:|")
+    print("\n".join(rows))
+    return 0
+
+
+def print_stats(d):
+    """Markdown table of rocprofv3's kernel_stats.csv (durations in microseconds)."""
+    import csv
+    import glob
+    fs = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    if not fs:
+        print(f"no kernel_stats.csv under {d}", file=sys.stderr)
+        return 1
+    print("| kernel | call | calls | avg us | min us | max us | total ms |")
+    print("|---|---|---:|---:|---:|---:|---:|")
+    with open(fs[0]) as fh:
+        for row in csv.DictReader(fh):
+            name = row["Name"]
+            short = name if len(name) <= 90 else name[:87] + "..."
+            print(f"| `{short}` | {_kernel_call(name) or ''} | {row['Calls']} | {float(row['AverageNs']) / 1e3:.1f} | "
+                  f"{float(row['MinNs']) / 1e3:.1f} | {float(row['MaxNs']) / 1e3:.1f} | "
+                  f"{float(row['TotalDurationNs']) / 1e6:.2f} |")
+    return 0
+
+
+def sweep_entry(c, tk, lam, s, m, w, kind):
+    import numpy as np
+    Mr = c.R * c.S * c.K
+    Lx = np.bincount(tk.ravel(), minlength=c.E).astype(np.float64)
+    ent = {"variant": kind, "B": c.B,
+           "maxvio": round(float((Lx.max() - Lx.mean()) / Lx.mean()), 3), "lambda": round(lam, 4),
+           "replicas": int(s[1]), "slot_replicas": int(s[2]), "fallback_replicas": int(s[3]),
+           "fallback_rows": int(s[4]), "migrated_frac": round(int(s[5]) / Mr, 4),
+           "migration_bound_frac": round(int(s[6]) / Mr, 4),
+           "rank_peak_over_mean": round(int(s[8]) / (c.S * c.K), 4),
+           "plan_us": round(m["plan"] * 1e3, 1), "prefetch_ms": round(m["prefetch"], 4),
+           "dispatch_ms": round(m["dispatch"], 4), "combine_ms": round(m["combine"], 4),
+           "dc_GBps": round((w["dispatch"][1] + w["combine"][1]) / ((m["dispatch"] + m["combine"]) / 1e3) / 1e9, 1)}
+    fwd = [k for k in ("gemm_gate_up", "gemm_down") if k in m]
+    if fwd:
+        fl = sum(w[k][1] for k in fwd)
+        t = sum(m[k] for k in fwd)
+    else:
+        fl = w["gemm_gate_up"][1] + w["gemm_down"][1]
+        t = m["ffn_fwd"]
+    ent["gemm_fwd_ms"] = round(t, 3)
+    ent["gemm_fwd_TFLOPs"] = round(fl / (t / 1e3) / 1e12, 1)
+    bwd = [k for k in ("gemm_dact", "gemm_dx", "gemm_dw2", "gemm_dw13") if k in m]
+    if bwd:
+        flb = sum(w[k][1] for k in bwd)
+        tb = sum(m[k] for k in bwd)
+        ent["gemm_bwd_ms"] = round(tb, 3)
+        ent["gemm_bwd_TFLOPs"] = round(flb / (tb / 1e3) / 1e12, 1)
+        ent["dc_bwd_GBps"] = round((w["dispatch_bwd"][1] + w["combine_bwd"][1]) /
+                                   ((m["dispatch_bwd"] + m["combine_bwd"]) / 1e3) / 1e9, 1)
+        ent["reduce_grad_ms"] = round(m["reduce_grad"], 4)
+    return ent
+
+
+def cpu_baseline(cfg, tokens, ngroups, log):
     """The CPU oracle, as it stands, on the same workload with `tokens` tokens per rank."""
     import numpy as np
     import oracle as O
@@ -275,7 +519,7 @@ def cpu_baseline(cfg, tokens, log):
     Mr = R * S * K
     dc_bytes = (R * S * H * 2 + Mr * H * 2 + 4 * Mr) + (Mr * H * 2 + 8 * Mr + R * S * H * 2)
     # expert FFN forward on the first few groups (weights drawn for those experts only)
-    grp = O.groups(plan)[:4]
+    grp = O.groups(plan)[:ngroups]
     rng = np.random.Generator(np.random.PCG64([c.seed, 99]))
     flops = 0.0
     t4 = time.perf_counter()
@@ -297,13 +541,13 @@ def cpu_baseline(cfg, tokens, log):
         "kind": "oracle",
         "sample": f"same workload with S={S} tokens/rank (R{R} E{E} K{K} H{H} maxvio {cfg.maxvio}): "
                   f"plan+destinations, dispatch and combine (value = their bytes / dispatch+combine time); "
-                  f"FFN forward on {len(grp)} groups in float64",
+                  f"FFN forward on {len(grp)} groups in float64 (ffn_TFLOPs)",
         "plan_s": round(t1 - t0, 3),
         "dispatch_s": round(t2 - t1, 3),
         "combine_s": round(t3 - t2, 3),
         "ffn_TFLOPs": round(flops / (t5 - t4) / 1e12, 4),
         "threads": os.environ.get("OMP_NUM_THREADS", str(cores)),
-        "cpu_model": platform.processor() or _cpu_model(),
+        "cpu_model": _cpu_model() or platform.processor(),
     }
     log("[bench] cpu baseline", res)
     return res
@@ -317,7 +561,7 @@ def _cpu_model():
                     return line.split(":", 1)[1].strip()
     except OSError:
         pass
-    return "unknown"
+    return ""
 
 
 if __name__ == "__main__":

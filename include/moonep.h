@@ -56,12 +56,24 @@ typedef struct moonep_dims {
     int32_t K;       /* experts per token, 1..min(E, 16)                            */
     int32_t H;       /* hidden size, multiple of 8                                  */
     int32_t I;       /* SwiGLU intermediate size, multiple of 8 (0 if no expert FFN) */
-    uint32_t flags;  /* MOONEP_TRAINING | MOONEP_F32_ROWS | MOONEP_GRAD_ACCUM      */
+    uint32_t flags;  /* MOONEP_TRAINING | MOONEP_F32_ROWS | MOONEP_GRAD_ACCUM | phases */
 } moonep_dims_t;
 
 #define MOONEP_TRAINING 1u   /* plan for training: a fallback replica sets MOONEP_ST_TRAIN_FALLBACK */
 #define MOONEP_F32_ROWS 2u   /* dispatch/combine rows are float32 instead of bf16 */
 #define MOONEP_GRAD_ACCUM 4u /* grouped_ffn_backward adds into dw*_home / dw*_red instead of writing them */
+
+/* Phase selection for the expert FFN calls.  Each phase is one GEMM kernel.  A call runs the
+ * phases of its own that are set in flags, in the order listed; with none of its phases set it
+ * runs all of them.  Bits of the other call are ignored.  Running phases in separate calls
+ * gives the same results as one call, provided the inputs a phase reads (noted) are in place:
+ * e.g. the weight-gradient phases may be deferred to overlap other work. */
+#define MOONEP_PHASE_GATE_UP 8u   /* grouped_ffn: [Gt U] = X W13, act = silu(Gt) U, gu_save  */
+#define MOONEP_PHASE_DOWN 16u     /* grouped_ffn: y = act W2 (reads act)                      */
+#define MOONEP_PHASE_DACT 32u     /* backward: dA = dY W2^T and SwiGLU' -> dGt|dU in gu_save  */
+#define MOONEP_PHASE_DX 64u       /* backward: drecv = [dGt dU] W13^T (reads dGt|dU)          */
+#define MOONEP_PHASE_DW2 128u     /* backward: dW2 = A^T dY                                   */
+#define MOONEP_PHASE_DW13 256u    /* backward: dW13 = X^T [dGt dU] (reads dGt|dU)             */
 
 enum {
     MOONEP_OK = 0,
@@ -146,7 +158,8 @@ int moonep_combine(const moonep_dims_t* dims, const int32_t* dest, const void* y
  *   recv    [R*S*K, H] bf16
  *   gu_save [R*S*K, 2I] bf16 out (Gt | U, kept for the backward) or NULL
  *   act     [R*S*K, I] bf16 out
- *   y       [R*S*K, H] bf16 out */
+ *   y       [R*S*K, H] bf16 out
+ * Phases (flags): MOONEP_PHASE_GATE_UP, MOONEP_PHASE_DOWN. */
 int moonep_grouped_ffn(const moonep_dims_t* dims, const void* plan_ws, const int32_t* cu_seqlens,
                        const void* recv, const void* w13_home, const void* w2_home,
                        const void* w13_slot, const void* w2_slot,
@@ -168,7 +181,10 @@ int moonep_grouped_ffn(const moonep_dims_t* dims, const void* plan_ws, const int
  *   Without MOONEP_GRAD_ACCUM the gradients are written (each home expert, including experts
  *   that received no rows, and each used slot); with it they are added to what the buffers
  *   hold (e.g. accumulation over micro-batches; the reduce slots are zero after
- *   moonep_reduce_grad). */
+ *   moonep_reduce_grad).
+ * Phases (flags): MOONEP_PHASE_DACT, MOONEP_PHASE_DX, MOONEP_PHASE_DW2, MOONEP_PHASE_DW13.
+ * gu_save holds Gt|U until MOONEP_PHASE_DACT has run and dGt|dU afterwards.  The two
+ * weight-gradient phases use tile counters in plan_ws: calls on one plan_ws must not overlap. */
 int moonep_grouped_ffn_backward(const moonep_dims_t* dims, const void* plan_ws,
                                 const int32_t* cu_seqlens, const void* recv,
                                 const void* gu_save, const void* act, const void* dy,

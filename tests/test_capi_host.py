@@ -66,7 +66,7 @@ def test_plan_rejects_null_and_misaligned():
     bad = _dims(E=255)
     assert lib.moonep_plan(ctypes.byref(bad), good, good, good, good, good, None) == EINVAL
     bad = _dims()
-    bad.flags = 64
+    bad.flags = 1024          # no such flag
     assert lib.moonep_plan(ctypes.byref(bad), good, good, good, good, good, None) == EINVAL
 
 
@@ -114,3 +114,16 @@ def test_python_binding_rejects_cpu_tensors():
     t = torch.zeros((2, 64, 2), dtype=torch.int32)
     with pytest.raises(ValueError, match="GPU tensor"):
         M.moonep_plan(d, t, t, t, t, t, stream=0)
+
+
+def test_flag_constants_match_header():
+    """The binding's flag and phase constants are the header's #define values."""
+    text = open(HEADER).read()
+    found = dict((k, int(v)) for k, v in re.findall(r"#define MOONEP_([A-Z0-9_]+) (\d+)u", text))
+    expect = {"TRAINING": M.TRAINING, "F32_ROWS": M.F32_ROWS, "GRAD_ACCUM": M.GRAD_ACCUM,
+              "PHASE_GATE_UP": M.PHASE_GATE_UP, "PHASE_DOWN": M.PHASE_DOWN, "PHASE_DACT": M.PHASE_DACT,
+              "PHASE_DX": M.PHASE_DX, "PHASE_DW2": M.PHASE_DW2, "PHASE_DW13": M.PHASE_DW13}
+    for k, v in expect.items():
+        assert found[k] == v, k
+    bits = [v for k, v in expect.items()]
+    assert len(set(bits)) == len(bits) and all(b & (b - 1) == 0 for b in bits)

@@ -145,6 +145,50 @@ def test_backward_writes_or_accumulates():
         assert not layer.dw13_red.any()
 
 
+def test_phases_match_single_call():
+    """Each phase flag runs one GEMM kernel; running the phases one call at a time (the weight
+    gradients deferred, dW13 before dW2) gives bit-identical results to one call."""
+    cfg = MID.with_(B=2)
+    topk, gates, xb, wb13, wb2, d, plan, dest, layer = _setup(cfg, training=True)
+    dout = bf16_from_bits(W.grad_rows(cfg.R, cfg.S, cfg.H, cfg.seed, "bf16"))
+    x, tk, g = bf16_from_bits(xb), i32(topk), f32(gates)
+    layer.forward(x, tk, g)
+    ref = {n: getattr(layer, n).clone() for n in ("gu", "act", "y")}
+    M.moonep_dispatch(d, layer.dest, dout, g, layer.dy)
+    M.moonep_grouped_ffn_backward(d, layer.ws, layer.cu, layer.recv, layer.gu, layer.act, layer.dy,
+                                  layer.w13, layer.w2, layer.w13_slot, layer.w2_slot, layer.drecv,
+                                  layer.dw13, layer.dw2, layer.dw13_red, layer.dw2_red)
+    ref.update({n: getattr(layer, n).clone() for n in ("drecv", "dw13", "dw2", "dw13_red", "dw2_red")})
+    ref["dgu"] = layer.gu.clone()
+    for n in ("act", "y", "gu", "drecv", "dw13", "dw2", "dw13_red", "dw2_red"):
+        getattr(layer, n).fill_(7.0)                  # stale content everywhere
+    for ph in (M.PHASE_GATE_UP, M.PHASE_DOWN):
+        M.moonep_grouped_ffn(d.with_flags(d.flags | ph), layer.ws, layer.cu, layer.recv, layer.w13,
+                             layer.w2, layer.w13_slot, layer.w2_slot, layer.gu, layer.act, layer.y)
+    torch.cuda.synchronize()
+    for n in ("gu", "act", "y"):
+        assert torch.equal(getattr(layer, n).view(torch.int16), ref[n].view(torch.int16)), n
+    for ph in (M.PHASE_DACT, M.PHASE_DX, M.PHASE_DW13, M.PHASE_DW2):
+        M.moonep_grouped_ffn_backward(d.with_flags(d.flags | ph), layer.ws, layer.cu, layer.recv, layer.gu,
+                                      layer.act, layer.dy, layer.w13, layer.w2, layer.w13_slot, layer.w2_slot,
+                                      layer.drecv, layer.dw13, layer.dw2, layer.dw13_red, layer.dw2_red)
+    torch.cuda.synchronize()
+    assert torch.equal(layer.gu.view(torch.int16), ref["dgu"].view(torch.int16))
+    assert torch.equal(layer.drecv.view(torch.int16), ref["drecv"].view(torch.int16))
+    for n in ("dw13", "dw2"):
+        assert torch.equal(getattr(layer, n), ref[n]), n
+    for en in plan.entries:                           # used reduce slots; the others are untouched
+        if en.w >= cfg.E:
+            assert torch.equal(layer.dw13_red[en.q, en.j], ref["dw13_red"][en.q, en.j])
+            assert torch.equal(layer.dw2_red[en.q, en.j], ref["dw2_red"][en.q, en.j])
+    # only the selected phase runs
+    layer.y.fill_(7.0)
+    M.moonep_grouped_ffn(d.with_flags(d.flags | M.PHASE_GATE_UP), layer.ws, layer.cu, layer.recv, layer.w13,
+                         layer.w2, layer.w13_slot, layer.w2_slot, layer.gu, layer.act, layer.y)
+    torch.cuda.synchronize()
+    assert bool((layer.y == 7.0).all())
+
+
 def test_tiny_layer_f32_rows():
     """Tiny configuration: fp32 token rows for dispatch/combine, bf16 expert GEMM."""
     cfg = W.CONFIGS["tiny"]
