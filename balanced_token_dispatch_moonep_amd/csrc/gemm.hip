@@ -11,8 +11,9 @@
 // Replica weight gradients go to the separate fp32 reduce buffer [TD, memory contract].
 //
 // Kernel design (MI355X / CDNA4):
-//   * 256x256 output tile per workgroup, 4 waves in 2x2, each wave 128x128 = 4x4 tiles
-//     of v_mfma_f32_32x32x16_bf16 (bf16 inputs, fp32 accumulation).  K step 32.
+//   * 256x256 output tile per workgroup, 8 waves in 2x4 (two per SIMD), each wave
+//     128x64 = 4x2 tiles of v_mfma_f32_32x32x16_bf16 (bf16 inputs, fp32 accumulation);
+//     a 4-wave 2x2 layout of 128x128 per wave is a compile-time alternative.  K step 32.
 //   * Operand tiles go HBM -> LDS with global_load_lds_dwordx4 (16 bytes per lane, no
 //     register staging), through a 4-stage ring: loads run three K steps ahead of the
 //     matrix cores; one explicit vmcnt wait and one barrier per step.
@@ -110,10 +111,6 @@ __device__ __forceinline__ int mn_pos(int k, int c) { return k * 32 + (c ^ ((k &
 // wait_vm() and a barrier before the data is read.  The instruction has no register outputs.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"   // m0 is reserved: nothing else in these kernels uses it
-// HBM -> LDS copy of 16 bytes per lane: lane l's bytes land at LDS byte address lds + 16*l (lds is
-// wave-uniform).  Issued as inline asm so the compiler does not track it as an LDS write (it would
-// otherwise drain every in-flight copy before each transposing LDS read); completion is awaited
-// with wait_vm() and a barrier before the data is read.  The instruction has no register outputs.
 __device__ __forceinline__ void dma16(const uint16_t* g, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
                  : "memory", "m0");
@@ -249,8 +246,11 @@ __device__ __forceinline__ void pipeline(f32x16_t (&acc)[4][WL<WN>::TN], char* s
         const char* st = smem + (s & (NSTAGE - 1)) * STAGE_BYTES;
         load_frags<A_KC, B_KC, EPI, WN>(f1, st, 1, wm, wn, lane);
         mma_frags<L::TN>(acc, f0);
-        // slice-1 fragments were read long ago; settling them here keeps the compiler from making
-        // the next MFMAs wait on the reads issued after the barrier
+        // Settle the slice-1 reads only after all slice-0 MFMAs are issued (the scheduling
+        // barrier keeps the compiler from hoisting the wait above them, which would expose the
+        // reads' latency); settling them here keeps the compiler from making the next MFMAs
+        // wait on the reads issued after the step barrier.
+        __builtin_amdgcn_sched_barrier(0);
         wait_lgkm0();
         if (s + 1 < nst) {
             // step s+1 must have landed: only step s+2 may still be in flight
