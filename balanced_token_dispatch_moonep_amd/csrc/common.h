@@ -69,6 +69,7 @@ struct PlanWs {
     int32_t* counters;     // [64] tile counters of dynamically scheduled kernels
     int32_t* dw_order;     // [E + R*B] dW targets by rows, descending (ties: lower id)
     uint16_t* zeros;       // [kZeroElems] zero bf16 row segment (source of masked GEMM tile loads)
+    int32_t* tile_pref;    // [2E + 1] prefix over the groups of their 256-row GEMM tiles
 };
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -109,6 +110,7 @@ inline size_t plan_ws_layout(const moonep_dims_t* d, void* base, PlanWs* ws) {
     w.counters = (int32_t*)take(64 * 4);
     w.dw_order = (int32_t*)take((E + RB) * 4);
     w.zeros = (uint16_t*)take(kZeroElems * 2);
+    w.tile_pref = (int32_t*)take((2 * E + 1) * 4);
     (void)R;
     if (ws) *ws = w;
     return off;

@@ -45,6 +45,14 @@ constexpr int BM = 256, BN = 256, BK = 32, NSTAGE = 4;
 constexpr int OP_BYTES = 256 * BK * 2;             // one operand tile of one stage: 16 KiB
 constexpr int STAGE_BYTES = 2 * OP_BYTES;
 constexpr int GEMM_SMEM = NSTAGE * STAGE_BYTES;    // 128 KiB
+// Row kernels: K step 64, so every k-contiguous row segment a DMA lane group fetches is one full
+// 128-byte line.
+constexpr int BK2 = 64;
+constexpr int OP2_BYTES = 256 * BK2 * 2;          // 32 KiB
+// One operand gets three buffers, the other two: five operand buffers of 32 KiB fill the 160 KiB
+// of LDS.  Which operand gets the third buffer is chosen per kernel by measurement (the SwiGLU
+// kernels: the activations; the plain-store kernels: the weights).
+constexpr int ROWS_SMEM = 5 * OP2_BYTES;          // 160 KiB
 constexpr int MAX_GROUPS = 2 * kMaxE;
 static_assert(4 * 32 * 132 * 4 <= GEMM_SMEM, "epilogue staging must fit in the stage ring");
 
@@ -104,6 +112,9 @@ __device__ __forceinline__ void wait_lgkm0() {
 __device__ __forceinline__ int kc_pos(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
 // m/n-contiguous tile [32 k][256 mn]: 16-byte chunk (k, c), c = mn/8 in 0..31
 __device__ __forceinline__ int mn_pos(int k, int c) { return k * 32 + (c ^ ((k & 3) << 2)); }
+// k-contiguous tile [256 rows][64 k]: 16-byte chunk (r, c), c = k/8 in 0..7; sixteen consecutive
+// rows reading the same chunk hit sixteen different 16-byte bank groups
+__device__ __forceinline__ int kc8_pos(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
 
 // HBM -> LDS copy of 16 bytes per lane: lane l's bytes land at lds + 16*l (lds is wave-uniform).
 // Issued as inline asm so the compiler does not track it as an LDS write (it would otherwise
@@ -125,6 +136,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 __device__ __forceinline__ bf16x8_t frag_kc(const char* T, int rb, int kk, int lane) {
     const int r = rb + (lane & 31), c = kk * 2 + (lane >> 5);
     return *reinterpret_cast<const bf16x8_t*>(T + kc_pos(r, c) * 16);
+}
+__device__ __forceinline__ bf16x8_t frag_kc8(const char* T, int rb, int kk, int lane) {
+    const int r = rb + (lane & 31), c = kk * 2 + (lane >> 5);
+    return *reinterpret_cast<const bf16x8_t*>(T + kc8_pos(r, c) * 16);
 }
 // same fragment from an m/n-contiguous tile: lane l gets column mb + l%32, k = 8*(l/32) + 0..7,
 // as two transposing reads of 4 k each (lanes of a 16-lane group address a 4 k x 16 col block)
@@ -269,6 +284,108 @@ __device__ __forceinline__ void pipeline(f32x16_t (&acc)[4][WL<WN>::TN], char* s
         }
     }
     block_sync();     // every wave is done with the ring before the epilogue reuses it
+}
+
+// Fragments of one 16-k slice (kk = 0..3) of a 64-k row-kernel stage.
+template <bool B_KC, int EPI, int WN>
+__device__ __forceinline__ void load_frags64(Frags<WL<WN>::TN>& f, const char* As, const char* Bs, int kk, int wm,
+                                             int wn, int lane) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) f.a[t] = frag_kc8(As, wm * 128 + t * 32, kk, lane);
+#pragma unroll
+    for (int t = 0; t < WL<WN>::TN; ++t)
+        f.b[t] = B_KC ? frag_kc8(Bs, bcol<EPI, WN>(wn, t), kk, lane) : frag_mn(Bs, bcol<EPI, WN>(wn, t), kk, lane);
+}
+
+// Main loop of the row kernels over nst 64-k stages.  A has RA buffers, B has RB (3 and 2, or 2
+// and 3 with DEEP_B; buffers of A at [0, RA), of B at [RA, RA+RB) in units of 32 KiB).  During stage s
+// the wave issues, after the barrier that retired stage s-1's buffers, the double-buffered
+// operand's stage s+1 (slice 0) and then the triple-buffered operand's stage s+2 (slice 1);
+// issue(op, u, buf, part) loads operand op (0 = A, 1 = B) of stage u into buffer buf.  At the
+// end of stage s only the triple-buffered operand's stage s+2 may be newer than stage s+1.
+// Fragments are double-buffered across the four 16-k slices, and the barrier sits before the
+// last slice's MFMAs so they cover the first reads of the next stage.
+template <bool B_KC, int EPI, int WN, bool DEEP_B, typename Issue>
+__device__ __forceinline__ void pipeline64(f32x16_t (&acc)[4][WL<WN>::TN], char* smem, int nst, int wm, int wn,
+                                           int lane, Issue&& issue) {
+    using L = WL<WN>;
+    constexpr int P2 = 2 * L::PARTS;      // loads per operand, stage and wave
+    constexpr int RA = DEEP_B ? 2 : 3, RB = DEEP_B ? 3 : 2;
+    constexpr int D2 = RA == 2 ? 0 : 1;   // double-buffered operand
+    constexpr int D3 = 1 - D2;            // triple-buffered operand
+    constexpr int N3 = D3 == 0 ? RA : RB;
+    auto buf_of = [&](int op, int u) { return op == 0 ? u % RA : RA + u % RB; };
+#pragma unroll
+    for (int p = 0; p < P2; ++p) issue(0, 0, buf_of(0, 0), p);
+#pragma unroll
+    for (int p = 0; p < P2; ++p) issue(1, 0, buf_of(1, 0), p);
+    if (nst > 1) {
+#pragma unroll
+        for (int p = 0; p < P2; ++p) issue(D3, 1, buf_of(D3, 1), p);
+        wait_vm<P2>();
+    } else {
+        wait_vm<0>();
+    }
+    block_sync();
+    Frags<L::TN> f0, f1;
+    load_frags64<B_KC, EPI, WN>(f0, smem, smem + RA * OP2_BYTES, 0, wm, wn, lane);
+    for (int s = 0; s < nst; ++s) {
+        const char* As = smem + (s % RA) * OP2_BYTES;
+        const char* Bs = smem + (RA + s % RB) * OP2_BYTES;
+        const bool more = s + 1 < nst, more3 = s + 2 < nst;
+        // slice 0: the double-buffered operand of stage s+1
+        load_frags64<B_KC, EPI, WN>(f1, As, Bs, 1, wm, wn, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            mma_row<L::TN>(acc, f0, i);
+            if (i % (4 / P2 > 0 ? 4 / P2 : 1) == 0 && more)
+#pragma unroll
+                for (int p = 0; p < (P2 > 4 ? P2 / 4 : 1); ++p) {
+                    const int part = P2 > 4 ? i * (P2 / 4) + p : i / (4 / P2);
+                    issue(D2, s + 1, buf_of(D2, s + 1), part);
+                }
+        }
+        // slice 1: the triple-buffered operand of stage s+2
+        load_frags64<B_KC, EPI, WN>(f0, As, Bs, 2, wm, wn, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            mma_row<L::TN>(acc, f1, i);
+            if (i % (4 / P2 > 0 ? 4 / P2 : 1) == 0 && more3)
+#pragma unroll
+                for (int p = 0; p < (P2 > 4 ? P2 / 4 : 1); ++p) {
+                    const int part = P2 > 4 ? i * (P2 / 4) + p : i / (4 / P2);
+                    issue(D3, s + 2, buf_of(D3, s + 2), part);
+                }
+        }
+        // slice 2
+        load_frags64<B_KC, EPI, WN>(f1, As, Bs, 3, wm, wn, lane);
+        mma_frags<L::TN>(acc, f0);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_lgkm0();
+        if (more) {
+            if (more3) wait_vm<P2>();     // stage s+1 has landed (stage s+2's deep operand may not)
+            else wait_vm<0>();
+            block_sync();
+            load_frags64<B_KC, EPI, WN>(f0, smem + ((s + 1) % RA) * OP2_BYTES,
+                                        smem + (RA + (s + 1) % RB) * OP2_BYTES, 0, wm, wn, lane);
+        }
+        // slice 3
+        mma_frags<L::TN>(acc, f1);
+    }
+    (void)N3;
+    block_sync();     // every wave is done with the buffers before the epilogue reuses them
+}
+
+// m-tile prefix of the groups (tile_pref[g] = 256-row tiles of groups before g), for the row kernels
+__global__ __launch_bounds__(64) void tile_prefix_kernel(PlanWs w) {
+    if (threadIdx.x != 0) return;
+    const int ng = min(max(w.hdr[HDR_NGROUPS], 0), 2 * w.E);
+    int run = 0;
+    for (int g = 0; g < ng; ++g) {
+        w.tile_pref[g] = run;
+        run += (group_rows(w.groups[g], w) + BM - 1) / BM;
+    }
+    w.tile_pref[ng] = run;
 }
 
 // ---------------------------------------------------------------------------
@@ -437,104 +554,74 @@ __device__ __forceinline__ void epi_dw_quarter(const GemmArgs& a, const f32x16_t
 template <int MODE, int EPI, int WN>
 __global__ __launch_bounds__(128 * WN, 1) void gemm_rows_kernel(GemmArgs a) {
     using L = WL<WN>;
-    constexpr int NTHR = L::NTHR;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
-    __shared__ int s_pref[MAX_GROUPS + 1];
-    __shared__ int s_part[NTHR];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
     const Group* groups = a.w.groups;
     const int ng = min(max(a.w.hdr[HDR_NGROUPS], 0), min(2 * a.w.E, MAX_GROUPS));
-
-    // m-tiles per group -> prefix in LDS (each thread scans a contiguous slice)
-    {
-        const int per = (ng + NTHR - 1) / NTHR;
-        const int lo = tid * per;
-        int sum = 0;
-        for (int g = lo; g < lo + per && g < ng; ++g) sum += (group_rows(groups[g], a.w) + BM - 1) / BM;
-        s_part[tid] = sum;
-        __syncthreads();
-        if (tid == 0) {
-            int run = 0;
-            for (int i = 0; i < NTHR; ++i) {
-                const int v = s_part[i];
-                s_part[i] = run;
-                run += v;
-            }
-        }
-        __syncthreads();
-        int run = s_part[tid];
-        for (int g = lo; g < lo + per && g < ng; ++g) {
-            s_pref[g] = run;
-            run += (group_rows(groups[g], a.w) + BM - 1) / BM;
-        }
-        if (tid == NTHR - 1) s_pref[ng] = run;
-        __syncthreads();
-    }
+    const int32_t* tp = a.w.tile_pref;    // m-tile prefix of the groups (tile_prefix_kernel)
     const int NT = a.ntiles_n;
-    const int total = s_pref[ng] * NT;
+    const int total = tp[ng] * NT;
     const int nxcd = 8;
     const int xcd = blockIdx.x % nxcd, li = blockIdx.x / nxcd, per_wg = gridDim.x / nxcd;
     const int chunk = (total + nxcd - 1) / nxcd;
     const int t_lo = xcd * chunk, t_hi = min(total, t_lo + chunk);
     float* ep = reinterpret_cast<float*>(smem) + wave * 32 * L::EPL;
-    const int nst = a.K / BK;
-    const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds_addr(smem) + wave * L::PARTS * 1024);
+    const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds_addr(smem) + wave * 2 * L::PARTS * 1024);
 
     for (int t = t_lo + li; t < t_hi; t += per_wg) {
         int lo = 0, hi = ng - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
-            if (s_pref[mid] * NT <= t) lo = mid; else hi = mid - 1;
+            if (tp[mid] * NT <= t) lo = mid; else hi = mid - 1;
         }
         const int g = lo;
         const Group gr = groups[g];
-        const int mtiles = s_pref[g + 1] - s_pref[g];
-        const int local = t - s_pref[g] * NT;
+        const int mtiles = tp[g + 1] - tp[g];
+        const int local = t - tp[g] * NT;
         const int nt = local / mtiles, mt = local % mtiles;
         const int row0 = gr.row0 + mt * BM;
         const int mvalid = min(BM, group_rows(gr, a.w) - mt * BM);
         const uint16_t* W = gr.wsel >= 0 ? a.Bhome + (size_t)gr.wsel * a.bstride
                                          : a.Bslot + (size_t)(-1 - gr.wsel) * a.bstride;
 
-        // per-lane sources of this wave's DMA loads (PARTS per operand and step)
-        const uint16_t* ap[L::PARTS];
-        const uint16_t* bp[L::PARTS];
-        bool bmove[L::PARTS];
+        // per-lane sources of this wave's DMA loads (2*PARTS per operand and stage), as element
+        // offsets from the operand base; rows and columns outside the tile clamp to the last valid
+        // one (their products only reach outputs the epilogue does not store)
+        constexpr int P2 = 2 * L::PARTS;
+        int ao[P2], bo[P2];
 #pragma unroll
-        for (int i = 0; i < L::PARTS; ++i) {
-            const int p = (wave * L::PARTS + i) * 64 + lane;
-            {   // A: k-contiguous activations, rows beyond the group clamp to its last row
-                const int r = p >> 2, c = (p & 3) ^ ((r >> 2) & 3);
-                ap[i] = a.A + (size_t)(row0 + min(r, mvalid - 1)) * a.lda + c * 8;
+        for (int i = 0; i < P2; ++i) {
+            const int p = (wave * P2 + i) * 64 + lane;
+            {   // A: k-contiguous activations [rows, K]
+                const int r = p >> 3, c = (p & 7) ^ ((r >> 1) & 7);
+                ao[i] = (row0 + min(r, mvalid - 1)) * a.lda + c * 8;
             }
             if (MODE == ROWS_BK) {   // weights [N, K]
-                const int r = p >> 2, c = (p & 3) ^ ((r >> 2) & 3);
-                const int n = nt * BN + r;
-                bmove[i] = n < a.N;
-                bp[i] = bmove[i] ? W + (size_t)n * a.ldb + c * 8 : a.w.zeros + c * 8;
+                const int r = p >> 3, c = (p & 7) ^ ((r >> 1) & 7);
+                bo[i] = min(nt * BN + r, a.N - 1) * a.ldb + c * 8;
             } else {                 // weights [K, N]
                 const int k = p >> 5, c = (p & 31) ^ ((k & 3) << 2);
                 int col;
                 if (EPI == EPI_SWIGLU_FWD) {
-                    const int cc = nt * 128 + (c & 15) * 8;
-                    bmove[i] = cc < a.I;
+                    const int cc = min(nt * 128 + (c & 15) * 8, a.I - 8);
                     col = c < 16 ? cc : a.I + cc;
                 } else {
-                    col = nt * BN + c * 8;
-                    bmove[i] = col < a.N;
+                    col = min(nt * BN + c * 8, a.N - 8);
                 }
-                bp[i] = bmove[i] ? W + (size_t)k * a.ldb + col : a.w.zeros + c * 8;
+                bo[i] = k * a.ldb + col;
             }
         }
-        const long long bstep = MODE == ROWS_BK ? (long long)BK : (long long)BK * a.ldb;
+        const int bstep = MODE == ROWS_BK ? BK2 : BK2 * a.ldb;
+        const uint16_t* A0 = a.A;
 
         f32x16_t acc[4][L::TN];
         zero_acc<L::TN>(acc);
-        pipeline<true, MODE == ROWS_BK, EPI, WN>(acc, smem, nst, wm, wn, lane, [&](int s, int buf, int i) {
-            const uint32_t l = lds_wave + buf * STAGE_BYTES + i * 1024;
-            dma16(ap[i] + (size_t)s * BK, l);
-            dma16(bmove[i] ? bp[i] + (size_t)s * bstep : bp[i], l + OP_BYTES);
+        pipeline64<MODE == ROWS_BK, EPI, WN, EPI == EPI_STORE>(acc, smem, a.K / BK2, wm, wn, lane,
+                                             [&](int op, int s, int buf, int i) {
+            const uint32_t l = lds_wave + buf * OP2_BYTES + i * 1024;
+            if (op == 0) dma16(A0 + (ao[i] + s * BK2), l);
+            else dma16(W + (bo[i] + s * bstep), l);
         });
         epi_rows_quarter<EPI, WN, 0>(a, acc, ep, wm, wn, lane, nt, row0, mvalid);
         epi_rows_quarter<EPI, WN, 1>(a, acc, ep, wm, wn, lane, nt, row0, mvalid);
@@ -686,7 +773,7 @@ static int launch_rows(int epi, int mode, const GemmArgs& a, hipStream_t s) {
     do {                                                                                               \
         static bool ok = set_smem(gemm_rows_kernel<M_, E_, WN>);                                       \
         if (!ok) return MOONEP_EHIP;                                                                   \
-        hipLaunchKernelGGL((gemm_rows_kernel<M_, E_, WN>), dim3(grid), dim3(128 * WN), GEMM_SMEM, s, a); \
+        hipLaunchKernelGGL((gemm_rows_kernel<M_, E_, WN>), dim3(grid), dim3(128 * WN), ROWS_SMEM, s, a); \
     } while (0)
     if (epi == EPI_SWIGLU_FWD && mode == ROWS_BN) MOONEP_ROWS(ROWS_BN, EPI_SWIGLU_FWD);
     else if (epi == EPI_STORE && mode == ROWS_BN) MOONEP_ROWS(ROWS_BN, EPI_STORE);
@@ -723,6 +810,8 @@ static int check_ffn_dims(const moonep_dims_t* d) {
     if (rc != MOONEP_OK) return rc;
     if (d->flags & MOONEP_F32_ROWS) return MOONEP_ENOTSUP;   // the expert GEMM is bf16
     if (d->H % 64 != 0 || d->I % 64 != 0) return MOONEP_ENOTSUP;
+    // the row kernels address operands with 32-bit element offsets
+    if ((long long)d->R * d->S * d->K * std::max(d->H, 2 * d->I) >= (1ll << 31)) return MOONEP_ENOTSUP;
     return MOONEP_OK;
 }
 
@@ -767,6 +856,8 @@ extern "C" int moonep_grouped_ffn(const moonep_dims_t* dims, const void* plan_ws
     a.gu = static_cast<uint16_t*>(gu_save);
     a.ntiles_n = (I + 127) / 128;
     const uint32_t ph = phases(dims, kFwdPhases);
+    hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(64), 0, s, a.w);
+    MOONEP_LAUNCH_CHECK();
     if (ph & MOONEP_PHASE_GATE_UP) {
         rc = launch_rows(EPI_SWIGLU_FWD, ROWS_BN, a, s);
         if (rc != MOONEP_OK) return rc;
@@ -819,6 +910,10 @@ extern "C" int moonep_grouped_ffn_backward(const moonep_dims_t* dims, const void
     plan_ws_layout(dims, const_cast<void*>(plan_ws), &a.w);
     uint16_t* gu = static_cast<uint16_t*>(const_cast<void*>(gu_save));
     const uint32_t ph = phases(dims, kBwdPhases);
+    if (ph & (MOONEP_PHASE_DACT | MOONEP_PHASE_DX)) {
+        hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(64), 0, s, a.w);
+        MOONEP_LAUNCH_CHECK();
+    }
     // dA = dY W2^T (B = W2 [I, H] is k-contiguous), fused SwiGLU' written over Gt|U
     a.A = static_cast<const uint16_t*>(dy);
     a.lda = H;
