@@ -753,9 +753,9 @@ static int num_cus() {
 }
 
 template <typename K>
-static bool set_smem(K kernel) {
+static bool set_smem(K kernel, int bytes) {
     return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, GEMM_SMEM) == hipSuccess;
+                               hipFuncAttributeMaxDynamicSharedMemorySize, bytes) == hipSuccess;
 }
 
 // waves along N of each kernel (2: 4 waves of 128x128; 4: 8 waves of 128x64)
@@ -771,7 +771,7 @@ static int launch_rows(int epi, int mode, const GemmArgs& a, hipStream_t s) {
     constexpr int WN = MOONEP_WN_ROWS;
 #define MOONEP_ROWS(M_, E_)                                                                            \
     do {                                                                                               \
-        static bool ok = set_smem(gemm_rows_kernel<M_, E_, WN>);                                       \
+        static bool ok = set_smem(gemm_rows_kernel<M_, E_, WN>, ROWS_SMEM);                            \
         if (!ok) return MOONEP_EHIP;                                                                   \
         hipLaunchKernelGGL((gemm_rows_kernel<M_, E_, WN>), dim3(grid), dim3(128 * WN), ROWS_SMEM, s, a); \
     } while (0)
@@ -789,7 +789,7 @@ static int launch_rows(int epi, int mode, const GemmArgs& a, hipStream_t s) {
 template <int WHICH>
 static int launch_dw(const GemmArgs& a, hipStream_t s) {
     constexpr int WN = MOONEP_WN_DW;
-    static bool ok = set_smem(gemm_dw_kernel<WN, WHICH>);
+    static bool ok = set_smem(gemm_dw_kernel<WN, WHICH>, GEMM_SMEM);
     if (!ok) return MOONEP_EHIP;
     hipLaunchKernelGGL(reset_counters_kernel, dim3(1), dim3(64), 0, s, a.counter, 1);
     MOONEP_LAUNCH_CHECK();
