@@ -20,8 +20,8 @@ __all__ = [
     "PHASE_GATE_UP", "PHASE_DOWN", "PHASE_DACT", "PHASE_DX", "PHASE_DW2", "PHASE_DW13",
     "ST_BAD_ID", "ST_DUP_ID", "ST_CAPACITY", "ST_OVERFLOW", "ST_TRAIN_FALLBACK",
     "moonep_plan_workspace_bytes", "moonep_plan", "moonep_prefetch", "moonep_dispatch",
-    "moonep_combine", "moonep_grouped_ffn", "moonep_grouped_ffn_backward", "moonep_reduce_grad",
-    "moonep_strerror", "moonep_version", "EXPORTED",
+    "moonep_combine", "moonep_dispatch_staged", "moonep_combine_staged", "moonep_grouped_ffn",
+    "moonep_grouped_ffn_backward", "moonep_reduce_grad", "moonep_strerror", "moonep_version", "EXPORTED",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoonep.so")
@@ -42,8 +42,8 @@ STAT_NAMES = (
 )
 EXPORTED = (
     "moonep_plan_workspace_bytes", "moonep_plan", "moonep_prefetch", "moonep_dispatch",
-    "moonep_combine", "moonep_grouped_ffn", "moonep_grouped_ffn_backward", "moonep_reduce_grad",
-    "moonep_strerror", "moonep_version",
+    "moonep_combine", "moonep_dispatch_staged", "moonep_combine_staged", "moonep_grouped_ffn",
+    "moonep_grouped_ffn_backward", "moonep_reduce_grad", "moonep_strerror", "moonep_version",
 )
 
 
@@ -85,6 +85,8 @@ def _load():
     L.moonep_prefetch.argtypes = [P, VP, VP, VP, VP, VP, VP]
     L.moonep_dispatch.argtypes = [P, VP, VP, VP, VP, VP]
     L.moonep_combine.argtypes = [P, VP, VP, VP, VP, VP]
+    L.moonep_dispatch_staged.argtypes = [P, VP, VP, VP, VP, VP, VP]
+    L.moonep_combine_staged.argtypes = [P, VP, VP, VP, VP, VP, VP]
     L.moonep_grouped_ffn.argtypes = [P, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP]
     L.moonep_grouped_ffn_backward.argtypes = [P] + [VP] * 16
     L.moonep_reduce_grad.argtypes = [P, VP, VP, VP, VP, VP, VP]
@@ -228,6 +230,36 @@ def moonep_combine(d: Dims, dest, y, gates, out, stream=None) -> None:
         _ptr(out, "out", rt, (d.R, d.S, d.H)),
     )
     _check(_lib().moonep_combine(ctypes.byref(d), *args, _stream(stream)), "moonep_combine")
+
+
+def moonep_dispatch_staged(d: Dims, dest, src, row_scale, stage, recv, stream=None) -> None:
+    """Non-zero-copy baseline of moonep_dispatch (arrival-order copy, then a sort-copy)."""
+    torch = _torch()
+    rt = _rows_dtype(d)
+    M = d.R * d.S * d.K
+    args = (
+        _ptr(dest, "dest", torch.int32, (d.R, d.S, d.K)),
+        _ptr(src, "src", rt, (d.R, d.S, d.H)),
+        _ptr(row_scale, "row_scale", torch.float32, (d.R, d.S, d.K), optional=True),
+        _ptr(stage, "stage", rt, (M, d.H)),
+        _ptr(recv, "recv", rt, (M, d.H)),
+    )
+    _check(_lib().moonep_dispatch_staged(ctypes.byref(d), *args, _stream(stream)), "moonep_dispatch_staged")
+
+
+def moonep_combine_staged(d: Dims, dest, y, gates, stage, out, stream=None) -> None:
+    """Non-zero-copy baseline of moonep_combine (gather to arrival order, then reduce)."""
+    torch = _torch()
+    rt = _rows_dtype(d)
+    M = d.R * d.S * d.K
+    args = (
+        _ptr(dest, "dest", torch.int32, (d.R, d.S, d.K)),
+        _ptr(y, "y", rt, (M, d.H)),
+        _ptr(gates, "gates", torch.float32, (d.R, d.S, d.K), optional=True),
+        _ptr(stage, "stage", rt, (M, d.H)),
+        _ptr(out, "out", rt, (d.R, d.S, d.H)),
+    )
+    _check(_lib().moonep_combine_staged(ctypes.byref(d), *args, _stream(stream)), "moonep_combine_staged")
 
 
 def moonep_grouped_ffn(d: Dims, plan_ws, cu_seqlens, recv, w13_home, w2_home, w13_slot, w2_slot,

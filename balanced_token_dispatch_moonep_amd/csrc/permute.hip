@@ -40,7 +40,8 @@ __device__ __forceinline__ uint4 scale_vec(uint4 v, float g) {
 }
 
 // recv[dest[p]] = scale(src[token(p)]); one wave per token, 16-byte vectors per lane.
-template <bool F32, bool SCALE, int VB>
+// IDENT: dest[p] = p (rows land in arrival order: the first copy of the staged baseline).
+template <bool F32, bool SCALE, int VB, bool IDENT = false>
 __global__ __launch_bounds__(256) void dispatch_kernel(const int32_t* __restrict__ dest,
                                                        const uint4* __restrict__ src,
                                                        const float* __restrict__ scale,
@@ -60,7 +61,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const int32_t* __restrict
             if (v < rowvec) x[u] = ld_nt(s + v);
         }
         for (int k = 0; k < K; ++k) {
-            const int d = dp[k];
+            const int d = IDENT ? tok * K + k : dp[k];
             if ((unsigned long long)(long long)d >= (unsigned long long)nrows) continue;
             const float g = SCALE ? gp[k] : 1.0f;
             uint4* o = recv + (size_t)d * rowvec;
@@ -94,7 +95,8 @@ __device__ __forceinline__ void acc_vec(float* a, uint4 v, float g) {
 
 // out[token] = sum_k g_k * y[dest[p_k]] (k order, float32); one wave per token.
 // KT > 0: compile-time K (all K loads of a vector batch issued before accumulating).
-template <bool F32, bool GATES, int KT, int VB>
+// IDENT: dest[p] = p (rows read in arrival order: the reduction of the staged baseline).
+template <bool F32, bool GATES, int KT, int VB, bool IDENT = false>
 __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ dest,
                                                       const uint4* __restrict__ y,
                                                       const float* __restrict__ gates,
@@ -118,7 +120,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
             uint4 x[KT > 0 ? KT : 1][VB];
 #pragma unroll
             for (int k = 0; k < (KT > 0 ? KT : 1); ++k) {
-                const int d = dp[k];
+                const int d = IDENT ? tok * K + k : dp[k];
                 const bool ok = (unsigned long long)(long long)d < (unsigned long long)nrows;
                 const uint4* yr = y + (size_t)(ok ? d : 0) * rowvec;
 #pragma unroll
@@ -135,7 +137,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
             }
         } else {
             for (int k = 0; k < K; ++k) {
-                const int d = dp[k];
+                const int d = IDENT ? tok * K + k : dp[k];
                 if ((unsigned long long)(long long)d >= (unsigned long long)nrows) continue;
                 const float g = GATES ? gp[k] : 1.0f;
                 const uint4* yr = y + (size_t)d * rowvec;
@@ -167,24 +169,52 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
     }
 }
 
-template <bool F32, bool GATES>
+template <bool F32, bool GATES, bool IDENT = false>
 static void launch_combine(int K, dim3 grid, hipStream_t s, const int32_t* dest, const uint4* y,
                            const float* gates, uint4* out, int ntok, int rowvec, long long nrows) {
     switch (K) {
         case 8:
-            hipLaunchKernelGGL((combine_kernel<F32, GATES, 8, 2>), grid, dim3(256), 0, s, dest, y, gates, out, ntok, K, rowvec, nrows);
+            hipLaunchKernelGGL((combine_kernel<F32, GATES, 8, 2, IDENT>), grid, dim3(256), 0, s, dest, y, gates, out, ntok, K, rowvec, nrows);
             break;
         case 4:
-            hipLaunchKernelGGL((combine_kernel<F32, GATES, 4, 4>), grid, dim3(256), 0, s, dest, y, gates, out, ntok, K, rowvec, nrows);
+            hipLaunchKernelGGL((combine_kernel<F32, GATES, 4, 4, IDENT>), grid, dim3(256), 0, s, dest, y, gates, out, ntok, K, rowvec, nrows);
             break;
         case 2:
-            hipLaunchKernelGGL((combine_kernel<F32, GATES, 2, 4>), grid, dim3(256), 0, s, dest, y, gates, out, ntok, K, rowvec, nrows);
+            hipLaunchKernelGGL((combine_kernel<F32, GATES, 2, 4, IDENT>), grid, dim3(256), 0, s, dest, y, gates, out, ntok, K, rowvec, nrows);
             break;
         case 1:
-            hipLaunchKernelGGL((combine_kernel<F32, GATES, 1, 4>), grid, dim3(256), 0, s, dest, y, gates, out, ntok, K, rowvec, nrows);
+            hipLaunchKernelGGL((combine_kernel<F32, GATES, 1, 4, IDENT>), grid, dim3(256), 0, s, dest, y, gates, out, ntok, K, rowvec, nrows);
             break;
         default:
-            hipLaunchKernelGGL((combine_kernel<F32, GATES, 0, 2>), grid, dim3(256), 0, s, dest, y, gates, out, ntok, K, rowvec, nrows);
+            hipLaunchKernelGGL((combine_kernel<F32, GATES, 0, 2, IDENT>), grid, dim3(256), 0, s, dest, y, gates, out, ntok, K, rowvec, nrows);
+    }
+}
+
+// The sort-copy of the staged baseline, one wave per row p, 16-byte vectors per lane:
+// GATHER: out[p] = in[dest[p]]; otherwise out[dest[p]] = in[p].
+template <bool GATHER>
+__global__ __launch_bounds__(256) void permute_rows_kernel(const int32_t* __restrict__ dest,
+                                                           const uint4* __restrict__ in, uint4* __restrict__ out,
+                                                           long long nrows, int rowvec) {
+    const long long p = (long long)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (p >= nrows) return;
+    const int d = dest[p];
+    if ((unsigned long long)(long long)d >= (unsigned long long)nrows) return;
+    const uint4* src = in + (size_t)(GATHER ? d : p) * rowvec;
+    uint4* dst = out + (size_t)(GATHER ? p : d) * rowvec;
+    for (int v0 = 0; v0 < rowvec; v0 += 64 * 4) {
+        uint4 x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int v = v0 + u * 64 + lane;
+            if (v < rowvec) x[u] = ld_nt(src + v);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int v = v0 + u * 64 + lane;
+            if (v < rowvec) st_nt(x[u], dst + v);
+        }
     }
 }
 
@@ -245,6 +275,78 @@ extern "C" int moonep_combine(const moonep_dims_t* dims, const int32_t* dest, co
     } else {
         if (gates) launch_combine<false, true>(dims->K, grid, s, dest, yv, gates, ov, ntok, rowvec, nrows);
         else launch_combine<false, false>(dims->K, grid, s, dest, yv, gates, ov, ntok, rowvec, nrows);
+    }
+    MOONEP_LAUNCH_CHECK();
+    return MOONEP_OK;
+}
+
+extern "C" int moonep_dispatch_staged(const moonep_dims_t* dims, const int32_t* dest, const void* src,
+                                      const float* row_scale, void* stage, void* recv, void* stream) {
+    const int rc = check_dims(dims, false);
+    if (rc != MOONEP_OK) return rc;
+    MOONEP_CHECK_PTR(dest);
+    MOONEP_CHECK_PTR(src);
+    MOONEP_CHECK_PTR(stage);
+    MOONEP_CHECK_PTR(recv);
+    if (row_scale && !aligned16(row_scale)) return MOONEP_EALIGN;
+    const bool f32 = (dims->flags & MOONEP_F32_ROWS) != 0;
+    const int ntok = dims->R * dims->S;
+    const int rowvec = dims->H * (f32 ? 4 : 2) / 16;
+    const long long nrows = (long long)ntok * dims->K;
+    const dim3 grid((ntok + kWavesPerBlock - 1) / kWavesPerBlock);
+    const dim3 rgrid((unsigned)((nrows + kWavesPerBlock - 1) / kWavesPerBlock));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint4* sv = static_cast<const uint4*>(src);
+    uint4* tv = static_cast<uint4*>(stage);
+    // 1. arrival order: stage[(r, s, k)] = scale(src[r, s])
+    if (f32) {
+        if (row_scale)
+            hipLaunchKernelGGL((dispatch_kernel<true, true, 4, true>), grid, dim3(256), 0, s, dest, sv, row_scale, tv, ntok, dims->K, rowvec, nrows);
+        else
+            hipLaunchKernelGGL((dispatch_kernel<true, false, 4, true>), grid, dim3(256), 0, s, dest, sv, row_scale, tv, ntok, dims->K, rowvec, nrows);
+    } else {
+        if (row_scale)
+            hipLaunchKernelGGL((dispatch_kernel<false, true, 4, true>), grid, dim3(256), 0, s, dest, sv, row_scale, tv, ntok, dims->K, rowvec, nrows);
+        else
+            hipLaunchKernelGGL((dispatch_kernel<false, false, 4, true>), grid, dim3(256), 0, s, dest, sv, row_scale, tv, ntok, dims->K, rowvec, nrows);
+    }
+    MOONEP_LAUNCH_CHECK();
+    // 2. the sort into expert order: recv[dest[p]] = stage[p]
+    hipLaunchKernelGGL((permute_rows_kernel<false>), rgrid, dim3(256), 0, s, dest, tv, static_cast<uint4*>(recv),
+                       nrows, rowvec);
+    MOONEP_LAUNCH_CHECK();
+    return MOONEP_OK;
+}
+
+extern "C" int moonep_combine_staged(const moonep_dims_t* dims, const int32_t* dest, const void* y,
+                                     const float* gates, void* stage, void* out, void* stream) {
+    const int rc = check_dims(dims, false);
+    if (rc != MOONEP_OK) return rc;
+    MOONEP_CHECK_PTR(dest);
+    MOONEP_CHECK_PTR(y);
+    MOONEP_CHECK_PTR(stage);
+    MOONEP_CHECK_PTR(out);
+    if (gates && !aligned16(gates)) return MOONEP_EALIGN;
+    const bool f32 = (dims->flags & MOONEP_F32_ROWS) != 0;
+    const int ntok = dims->R * dims->S;
+    const int rowvec = dims->H * (f32 ? 4 : 2) / 16;
+    const long long nrows = (long long)ntok * dims->K;
+    const dim3 grid((ntok + kWavesPerBlock - 1) / kWavesPerBlock);
+    const dim3 rgrid((unsigned)((nrows + kWavesPerBlock - 1) / kWavesPerBlock));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint4* tv = static_cast<uint4*>(stage);
+    // 1. back to arrival order: stage[p] = y[dest[p]]
+    hipLaunchKernelGGL((permute_rows_kernel<true>), rgrid, dim3(256), 0, s, dest, static_cast<const uint4*>(y), tv,
+                       nrows, rowvec);
+    MOONEP_LAUNCH_CHECK();
+    // 2. reduction over k in arrival order (same arithmetic as moonep_combine)
+    uint4* ov = static_cast<uint4*>(out);
+    if (f32) {
+        if (gates) launch_combine<true, true, true>(dims->K, grid, s, dest, tv, gates, ov, ntok, rowvec, nrows);
+        else launch_combine<true, false, true>(dims->K, grid, s, dest, tv, gates, ov, ntok, rowvec, nrows);
+    } else {
+        if (gates) launch_combine<false, true, true>(dims->K, grid, s, dest, tv, gates, ov, ntok, rowvec, nrows);
+        else launch_combine<false, false, true>(dims->K, grid, s, dest, tv, gates, ov, ntok, rowvec, nrows);
     }
     MOONEP_LAUNCH_CHECK();
     return MOONEP_OK;

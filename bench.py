@@ -244,6 +244,40 @@ def main():
         log("[bench] sweep", sweep[-1])
         del Li
 
+    # ---- zero-copy ablation: the staged baseline (arrival-order copy + sort-copy) ------------
+    ablation = None
+    if not args.no_sweep:
+        stage = torch.empty_like(L.recv)
+        T3 = Timer(torch)
+        for it in range(4):
+            T3.run("dispatch", lambda: L.dispatch(x))
+            T3.run("dispatch_staged", lambda: M.moonep_dispatch_staged(d, L.dest, x, None, stage, L.recv))
+            T3.run("combine", lambda: L.combine(g))
+            T3.run("combine_staged", lambda: M.moonep_combine_staged(d, L.dest, L.y, g, stage, L.out))
+            if it == 0:
+                torch.cuda.synchronize()
+                T3.clear()
+        torch.cuda.synchronize()
+        m3 = T3.avg_ms()
+        del stage
+        Mr = R * S * K
+        xb_, rb_ = R * S * H * 2, Mr * H * 2
+        moved_d = (xb_ + rb_) + (4.0 * Mr + 2 * rb_)            # arrival-order copy, then the sort-copy
+        moved_c = (4.0 * Mr + 2 * rb_) + (rb_ + 4.0 * Mr + xb_)  # gather back, then the reduction
+        alg = work["dispatch"][1] + work["combine"][1]
+        ablation = {
+            "fused_ms": round(m3["dispatch"] + m3["combine"], 4),
+            "staged_ms": round(m3["dispatch_staged"] + m3["combine_staged"], 4),
+            "dispatch_ms": round(m3["dispatch"], 4), "dispatch_staged_ms": round(m3["dispatch_staged"], 4),
+            "combine_ms": round(m3["combine"], 4), "combine_staged_ms": round(m3["combine_staged"], 4),
+            "algorithmic_GB": round(alg / 1e9, 3), "staged_moved_GB": round((moved_d + moved_c) / 1e9, 3),
+            "fused_GBps": round(alg / ((m3["dispatch"] + m3["combine"]) / 1e3) / 1e9, 1),
+            "staged_moved_GBps": round((moved_d + moved_c) / ((m3["dispatch_staged"] + m3["combine_staged"]) / 1e3)
+                                       / 1e9, 1),
+            "speedup": round((m3["dispatch_staged"] + m3["combine_staged"]) / (m3["dispatch"] + m3["combine"]), 3),
+        }
+        log("[bench] zero-copy ablation", ablation)
+
     # ---- CPU oracle baseline on a bounded sample of the same workload ----------------------
     cpu = None
     if not args.no_cpu:
@@ -275,6 +309,7 @@ def main():
         "roofline": roofline,
         "rooflines": rooflines,
         "sweep": sweep,
+        "zero_copy_ablation": ablation,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -150,6 +150,19 @@ int moonep_dispatch(const moonep_dims_t* dims, const int32_t* dest, const void* 
 int moonep_combine(const moonep_dims_t* dims, const int32_t* dest, const void* y,
                    const float* gates, void* out, void* stream);
 
+/* Staged (not zero-copy) permute and unpermute, the baseline that measures what sender-side
+ * final positions save [TC, "What the technique is"; AT, Technical Details; AL, Highlights]:
+ * rows first land in arrival order, stage[(r, s, k)] = scale(src[r, s]), and a separate
+ * sort-copy then moves them to their expert-grouped rows, recv[dest[p]] = stage[p].  Combine
+ * mirrors it: stage[p] = y[dest[p]], then out[r, s] = sum over k of gates * stage[(r, s, k)].
+ * Results are bit-identical to moonep_dispatch / moonep_combine; every row crosses HBM twice more.
+ *   stage [R*S*K, H] scratch of the row type (contents on return: the arrival-order rows)
+ *   other arguments as for moonep_dispatch / moonep_combine. */
+int moonep_dispatch_staged(const moonep_dims_t* dims, const int32_t* dest, const void* src,
+                           const float* row_scale, void* stage, void* recv, void* stream);
+int moonep_combine_staged(const moonep_dims_t* dims, const int32_t* dest, const void* y,
+                          const float* gates, void* stage, void* out, void* stream);
+
 /* Grouped SwiGLU expert FFN over the receive buffer [TC, flowchart "Group GEMM"; TD, memory
  * contract: cu_seqlens selects the active weight rows].  For each group (rank q, weight row w)
  * with rows X_g:  [Gt U] = X_g W13[w];  A = silu(Gt) * U;  Y_g = A W2[w]; bf16 inputs, float32

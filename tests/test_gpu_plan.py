@@ -234,3 +234,67 @@ def test_round_trip_full_size(maxvio):
         ref = sum(float(gates[r, s, k]) * W.bf16_to_f32(xb[r, s]).astype(np.float64) for k in range(cfg.K))
         got = f64_of(out[r, s])
         assert np.linalg.norm(got - ref) <= 1e-2 * np.linalg.norm(ref)
+
+
+# ----------------------------------------------------------------------------
+# staged (non-zero-copy) baseline: same results as the fused calls
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,over,scaled", [
+    ("tiny", {}, False), ("tiny", {"S": 100, "lam": 2.0}, True),
+    ("skew", {"S": 192, "H": 1032, "maxvio": 8.0}, True), ("balanced", {"S": 128, "H": 512, "K": 3}, False),
+])
+def test_staged_matches_fused(name, over, scaled):
+    cfg = W.CONFIGS[name].with_(**over)
+    topk, gates, x, d, plan, dest, dd = _layer_inputs(cfg)
+    say("staged", name, over, scaled)
+    xt = rows_tensor(x)
+    g = f32(gates)
+    M_ = cfg.R * cfg.C
+    recv = torch.empty((M_, cfg.H), dtype=xt.dtype, device=DEV)
+    recv2 = torch.full_like(recv, float("nan"))
+    stage = torch.full_like(recv, float("nan"))
+    M.moonep_dispatch(d, dd, xt, g if scaled else None, recv)
+    M.moonep_dispatch_staged(d, dd, xt, g if scaled else None, stage, recv2)
+    torch.cuda.synchronize()
+    asbits = (lambda t: t.cpu().numpy()) if cfg.dtype == "f32" else bits_of
+    assert asbits(recv2).tobytes() == asbits(recv).tobytes()
+    if not scaled:   # arrival order: row (r, s, k) holds token (r, s)
+        ref = np.repeat(x.reshape(cfg.R * cfg.S, cfg.H), cfg.K, axis=0)
+        assert asbits(stage).tobytes() == np.ascontiguousarray(ref).tobytes()
+        assert asbits(recv2).tobytes() == O.dispatch(dest, x).tobytes()
+    rng = np.random.default_rng(3)
+    yv = rng.standard_normal((M_, cfg.H)).astype(np.float32)
+    y = rows_tensor(yv if cfg.dtype == "f32" else W.bf16_bits(yv))
+    out = torch.empty((cfg.R, cfg.S, cfg.H), dtype=xt.dtype, device=DEV)
+    out2 = torch.full_like(out, float("nan"))
+    M.moonep_combine(d, dd, y, g, out)
+    M.moonep_combine_staged(d, dd, y, g, stage, out2)
+    torch.cuda.synchronize()
+    assert asbits(out2).tobytes() == asbits(out).tobytes()
+    # the gather to arrival order: stage[p] = y[dest[p]]
+    idx = torch.from_numpy(dest.reshape(-1).astype(np.int64)).to(DEV)
+    assert torch.equal(stage.view(torch.int16) if cfg.dtype != "f32" else stage,
+                       (y[idx].view(torch.int16) if cfg.dtype != "f32" else y[idx]))
+
+
+def test_staged_full_size_matches_fused():
+    cfg = W.CONFIGS["skew"].with_(maxvio=4.0)
+    topk, gates, _ = W.routing_for(cfg)
+    d = dims_of(cfg)
+    say("staged full size")
+    _, cu, dd, st = run_plan(d, topk)
+    x = bf16_from_bits(W.hidden_rows(cfg.R, cfg.S, cfg.H, cfg.seed, "bf16"))
+    g = f32(gates)
+    recv = torch.empty((cfg.R * cfg.C, cfg.H), dtype=torch.bfloat16, device=DEV)
+    recv2 = torch.empty_like(recv)
+    stage = torch.empty_like(recv)
+    M.moonep_dispatch(d, dd, x, None, recv)
+    M.moonep_dispatch_staged(d, dd, x, None, stage, recv2)
+    out = torch.empty_like(x)
+    out2 = torch.empty_like(x)
+    M.moonep_combine(d, dd, recv, g, out)
+    M.moonep_combine_staged(d, dd, recv2, g, stage, out2)
+    torch.cuda.synchronize()
+    assert torch.equal(recv.view(torch.int16), recv2.view(torch.int16))
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
