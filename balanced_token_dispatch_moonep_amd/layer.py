@@ -19,6 +19,50 @@ from . import (Dims, moonep_combine, moonep_dispatch, moonep_grouped_ffn,
                moonep_prefetch, moonep_reduce_grad, NSTATS)
 
 
+def _slot_shapes(R, B, H, I):
+    return (R, B, H, 2 * I), (R, B, I, H)
+
+
+def _nbytes(shape, itemsize):
+    n = itemsize
+    for v in shape:
+        n *= v
+    return n
+
+
+class MoonEPPool:
+    """Process-global prefetch slots shared by every layer [AT, TL;DR; TD, memory contract].
+
+    Layers run one after another, so one set of B weight slots per rank (and, in training,
+    one fp32 reduce buffer [R, B, ...]) serves all of them: the extra memory does not grow
+    with depth.  A layer whose slots were overwritten by later layers prefetches its replicas
+    again before its backward (its plan stays in its own workspace).
+    """
+
+    def __init__(self, R, B, H, I, training=False, device="cuda"):
+        dev = torch.device(device)
+        s13, s2 = _slot_shapes(R, B, H, I)
+        self.R, self.B, self.H, self.I, self.training = R, B, H, I, training
+        self.w13_slot = torch.zeros(s13, dtype=torch.bfloat16, device=dev) if B else None
+        self.w2_slot = torch.zeros(s2, dtype=torch.bfloat16, device=dev) if B else None
+        self.dw13_red = torch.zeros(s13, dtype=torch.float32, device=dev) if B and training else None
+        self.dw2_red = torch.zeros(s2, dtype=torch.float32, device=dev) if B and training else None
+        self.owner = None     # the layer whose replicas the slots hold
+
+    @staticmethod
+    def nbytes(R, B, H, I, training=False) -> dict:
+        s13, s2 = _slot_shapes(R, B, H, I)
+        slots = _nbytes(s13, 2) + _nbytes(s2, 2) if B else 0
+        red = _nbytes(s13, 4) + _nbytes(s2, 4) if B and training else 0
+        return {"prefetch": slots, "reduce": red, "total": slots + red}
+
+
+def stack_slot_bytes(R, B, H, I, layers, pooled, training=False) -> int:
+    """Bytes of prefetch slots (and reduce buffers) for `layers` layers, pooled or one set each."""
+    per = MoonEPPool.nbytes(R, B, H, I, training)["total"]
+    return per if pooled else layers * per
+
+
 class MoonEPLayer:
     """One emulated EP layer: R ranks as R static partitions of one GPU's memory.
 
@@ -27,9 +71,10 @@ class MoonEPLayer:
     planning, dispatch and combine run.
     """
 
-    def __init__(self, dims: Dims, w13=None, w2=None, training: bool = False, device="cuda"):
+    def __init__(self, dims: Dims, w13=None, w2=None, training: bool = False, device="cuda", pool=None):
         self.d = dims
         self.training = training
+        self.pool = pool
         dev = torch.device(device)
         self.device = dev
         R, E, B, S, K, H, I = dims.R, dims.E, dims.B, dims.S, dims.K, dims.H, dims.I
@@ -45,8 +90,13 @@ class MoonEPLayer:
         self.w13, self.w2 = w13, w2
         if I > 0:
             bf = torch.bfloat16
-            self.w13_slot = torch.zeros((R, B, H, 2 * I), dtype=bf, device=dev) if B else None
-            self.w2_slot = torch.zeros((R, B, I, H), dtype=bf, device=dev) if B else None
+            if pool is not None:
+                if (pool.R, pool.B, pool.H, pool.I) != (R, B, H, I) or (training and not pool.training):
+                    raise ValueError("the pool's shapes do not match the layer")
+                self.w13_slot, self.w2_slot = pool.w13_slot, pool.w2_slot
+            else:
+                self.w13_slot = torch.zeros((R, B, H, 2 * I), dtype=bf, device=dev) if B else None
+                self.w2_slot = torch.zeros((R, B, I, H), dtype=bf, device=dev) if B else None
             self.gu = torch.empty((M, 2 * I), dtype=bf, device=dev)
             self.act = torch.empty((M, I), dtype=bf, device=dev)
             self.y = torch.empty((M, H), dtype=bf, device=dev)
@@ -57,8 +107,11 @@ class MoonEPLayer:
                 self.dx = torch.empty((R, S, H), dtype=bf, device=dev)
                 self.dw13 = torch.zeros((E, H, 2 * I), dtype=f32, device=dev)
                 self.dw2 = torch.zeros((E, I, H), dtype=f32, device=dev)
-                self.dw13_red = torch.zeros((R, B, H, 2 * I), dtype=f32, device=dev) if B else None
-                self.dw2_red = torch.zeros((R, B, I, H), dtype=f32, device=dev) if B else None
+                if pool is not None:
+                    self.dw13_red, self.dw2_red = pool.dw13_red, pool.dw2_red
+                else:
+                    self.dw13_red = torch.zeros((R, B, H, 2 * I), dtype=f32, device=dev) if B else None
+                    self.dw2_red = torch.zeros((R, B, I, H), dtype=f32, device=dev) if B else None
         else:
             self.y = self.recv          # identity experts
 
@@ -69,6 +122,8 @@ class MoonEPLayer:
     def prefetch(self):
         if self.d.I > 0 and self.d.B > 0:
             moonep_prefetch(self.d, self.ws, self.w13, self.w2, self.w13_slot, self.w2_slot)
+            if self.pool is not None:
+                self.pool.owner = self
 
     def dispatch(self, x):
         moonep_dispatch(self.d, self.dest, x, None, self.recv)
@@ -96,6 +151,8 @@ class MoonEPLayer:
 
         The saved gate|up activations are overwritten by their gradients."""
         assert self.training and self.d.I > 0
+        if self.pool is not None and self.pool.owner is not self:
+            self.prefetch()       # a later layer reused the shared slots
         moonep_dispatch(self.d, self.dest, dout, gates, self.dy)
         moonep_grouped_ffn_backward(self.d, self.ws, self.cu, self.recv, self.gu, self.act, self.dy,
                                     self.w13, self.w2, self.w13_slot, self.w2_slot, self.drecv,

@@ -244,6 +244,47 @@ def main():
         log("[bench] sweep", sweep[-1])
         del Li
 
+    # ---- lognormal expert popularity (the planner workload of the thakicloud.com post) -------
+    lognormal = None
+    if not args.no_sweep:
+        c = W.LOGNORMAL
+        dl = M.Dims.make(c["R"], c["E"], B, c["S"], c["K"], H)
+        Ll = MoonEPLayer(dl, training=False)
+        xl = torch.randn((c["R"], c["S"], H), device=dev).to(torch.bfloat16)
+        with open(os.path.join(ROOT, "tests", "golden", "lognormal_table1.json")) as f:
+            post = {row[0]: row for row in json.load(f)["rows"]}
+        lognormal = []
+        for sg in c["sigmas"]:
+            tkl, gl = W.lognormal_routing(c["R"], c["S"], c["E"], c["K"], sg)
+            tkd, gd = torch.from_numpy(np.array(tkl)).to(dev), torch.from_numpy(gl).to(dev)
+            T4 = Timer(torch)
+            for it in range(4):
+                T4.run("plan", lambda: Ll.plan(tkd))
+                T4.run("dispatch", lambda: Ll.dispatch(xl))
+                T4.run("combine", lambda: Ll.combine(gd))
+                if it == 0:
+                    torch.cuda.synchronize()
+                    T4.clear()
+            torch.cuda.synchronize()
+            m4 = T4.avg_ms()
+            s4 = Ll.stats.cpu().numpy()
+            cap = c["S"] * c["K"]
+            rows_l = c["R"] * cap
+            dcb = 2 * (c["R"] * c["S"] * H * 2 + rows_l * H * 2) + 12.0 * rows_l
+            p = post.get(sg)
+            lognormal.append({
+                "sigma": sg, "baseline_peak_load": int(s4[8]), "baseline_min_load": int(s4[9]),
+                "peak_over_mean": round(int(s4[8]) / cap, 3), "moonep_peak_over_mean": 1.0,
+                "migrated_pct": round(100.0 * int(s4[5]) / rows_l, 2),
+                "migration_bound_pct": round(100.0 * int(s4[6]) / rows_l, 2),
+                "copies": int(s4[1]), "fallback": int(s4[3]), "plan_us": round(m4["plan"] * 1e3, 1),
+                "dc_GBps": round(dcb / ((m4["dispatch"] + m4["combine"]) / 1e3) / 1e9, 1),
+                "post_table1": None if p is None else {"peak_over_mean": p[3], "migrated_pct": p[5],
+                                                       "copy_slots": p[6]},
+            })
+            log("[bench] lognormal", lognormal[-1])
+        del Ll, xl
+
     # ---- zero-copy ablation: the staged baseline (arrival-order copy + sort-copy) ------------
     ablation = None
     if not args.no_sweep:
@@ -278,6 +319,16 @@ def main():
         }
         log("[bench] zero-copy ablation", ablation)
 
+    # ---- process-global prefetch pool: slot memory across depth, and its re-prefetch cost ----
+    from balanced_token_dispatch_moonep_amd.layer import MoonEPPool, stack_slot_bytes
+    pool = {
+        "per_set_GB": round(MoonEPPool.nbytes(R, B, H, I, training=True)["total"] / 1e9, 3),
+        "layers": {str(n): {"pooled_GB": round(stack_slot_bytes(R, B, H, I, n, True, True) / 1e9, 3),
+                            "per_layer_GB": round(stack_slot_bytes(R, B, H, I, n, False, True) / 1e9, 3)}
+                   for n in (1, 8, 64)},
+        "re_prefetch_ms_per_layer": round(ms["prefetch"], 4),
+    }
+
     # ---- CPU oracle baseline on a bounded sample of the same workload ----------------------
     cpu = None
     if not args.no_cpu:
@@ -310,6 +361,8 @@ def main():
         "rooflines": rooflines,
         "sweep": sweep,
         "zero_copy_ablation": ablation,
+        "lognormal_planner": lognormal,
+        "prefetch_pool": pool,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -127,3 +127,18 @@ def test_flag_constants_match_header():
         assert found[k] == v, k
     bits = [v for k, v in expect.items()]
     assert len(set(bits)) == len(bits) and all(b & (b - 1) == 0 for b in bits)
+
+
+def test_pool_bytes_match_memory_contract():
+    """One rank's pooled slot and reduce buffers are the memory contract's prefetch and fp32
+    reduce buffers (pinned to the thakicloud.com post's Table 2 through the oracle), and
+    pooling keeps them constant in depth."""
+    import oracle as O
+    from balanced_token_dispatch_moonep_amd.layer import MoonEPPool, stack_slot_bytes
+    for B, training in ((4, False), (32, True)):
+        got = MoonEPPool.nbytes(1, B, 7168, 2048, training)
+        ref = O.buffer_bytes(B, 4096, 8, 7168, 2048, training=training)
+        assert got["prefetch"] == ref["prefetch"] and got["reduce"] == ref["reduce"]
+    one = stack_slot_bytes(8, 4, 7168, 2048, 1, pooled=True, training=True)
+    assert stack_slot_bytes(8, 4, 7168, 2048, 61, pooled=True, training=True) == one
+    assert stack_slot_bytes(8, 4, 7168, 2048, 61, pooled=False, training=True) == 61 * one

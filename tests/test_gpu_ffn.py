@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import balanced_token_dispatch_moonep_amd as M
-from balanced_token_dispatch_moonep_amd.layer import MoonEPLayer
+from balanced_token_dispatch_moonep_amd.layer import MoonEPLayer, MoonEPPool
 import oracle as O
 import workload as W
 
@@ -308,3 +308,48 @@ def test_full_layer_backward_experts():
         say(f"  expert {e} (L={plan.L[e]}): dW13 {e13:.3e} dW2 {e2:.3e}")
         assert e13 <= TOL and e2 <= TOL
     assert not layer.dw13_red.any() and not layer.dw2_red.any()
+
+
+def test_layer_stack_with_shared_pool():
+    """Three layers sharing one prefetch pool give bit-identical outputs and gradients to three
+    layers with their own slots (each pooled layer prefetches again before its backward), and
+    the pooled stack allocates two pools' worth less memory."""
+    cfg = MID.with_(B=2)
+    layers_n = 3
+    topk, gates, _ = W.routing_for(cfg)
+    tk, g = i32(topk), f32(gates)
+    xb = bf16_from_bits(W.hidden_rows(cfg.R, cfg.S, cfg.H, cfg.seed, "bf16"))
+    dout = bf16_from_bits(W.grad_rows(cfg.R, cfg.S, cfg.H, cfg.seed, "bf16"))
+    ws = []
+    for l in range(layers_n):
+        w13f, w2f = W.expert_weights_np(cfg.E, cfg.H, cfg.I, cfg.seed + 10 + l)
+        ws.append((bf16_from_bits(W.bf16_bits(w13f)), bf16_from_bits(W.bf16_bits(w2f))))
+    d = M.Dims.make(cfg.R, cfg.E, cfg.B, cfg.S, cfg.K, cfg.H, cfg.I, training=True)
+
+    def run(pool):
+        torch.cuda.synchronize()
+        before = torch.cuda.memory_allocated()
+        if pool:
+            p = MoonEPPool(cfg.R, cfg.B, cfg.H, cfg.I, training=True, device=DEV)
+        stack = [MoonEPLayer(d, w13=a, w2=b, training=True, pool=p if pool else None) for a, b in ws]
+        torch.cuda.synchronize()
+        used = torch.cuda.memory_allocated() - before
+        h = xb
+        for L in stack:                     # forward through the stack (router output reused)
+            h = L.forward(h, tk, g).clone()
+        dh = dout
+        for L in reversed(stack):           # backward in reverse layer order
+            dh = L.backward(dh, g).clone()
+        torch.cuda.synchronize()
+        res = [h, dh] + [t.clone() for L in stack for t in (L.dw13, L.dw2)]
+        return res, used
+
+    ref, used_own = run(False)
+    got, used_pool = run(True)
+    for a, b in zip(ref, got):
+        assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a.view(torch.int16),
+                           b.view(torch.int32) if b.dtype == torch.float32 else b.view(torch.int16))
+    saved = used_own - used_pool
+    expect = (layers_n - 1) * MoonEPPool.nbytes(cfg.R, cfg.B, cfg.H, cfg.I, training=True)["total"]
+    say(f"  pooled stack saves {saved / 2**20:.1f} MiB (expected {expect / 2**20:.1f} MiB)")
+    assert abs(saved - expect) <= 2 * 2**20

@@ -298,3 +298,14 @@ def test_staged_full_size_matches_fused():
     torch.cuda.synchronize()
     assert torch.equal(recv.view(torch.int16), recv2.view(torch.int16))
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+@pytest.mark.parametrize("sigma", [0.0, 0.5, 1.0, 2.0, 5.0])
+def test_plan_lognormal(sigma):
+    """The planner workload of the thakicloud.com post (Table 1 setup), bit-exact to the oracle."""
+    c = W.LOGNORMAL
+    topk, _ = W.lognormal_routing(c["R"], c["S"], c["E"], c["K"], sigma)
+    d = M.Dims.make(c["R"], c["E"], 4, c["S"], c["K"], 128)
+    say("plan lognormal sigma", sigma)
+    plan, dest, (ws, cu, dd, st) = assert_plan_parity(d, np.array(topk))
+    assert np.all(cu.cpu().numpy()[:, -1] == c["S"] * c["K"])

@@ -282,3 +282,49 @@ def test_memory_table2():
             assert abs(b[k] / gib - row[k + "_gib"]) <= 0.0051, (row["mode"], k)
     hb = O.buffer_bytes(0, sh["S"], sh["K"], sh["H"], sh["I"], E_home=32)["home_weights"] / gib
     assert abs(hb - g["home_weights_gib_per_rank_E_over_R_32"]) < 0.05
+
+
+# ----------------------------------------------------------------------------
+# lognormal expert popularity (thakicloud.com post, "What we measured", Table 1 setup)
+# ----------------------------------------------------------------------------
+
+def _table1():
+    with open(os.path.join(os.path.dirname(__file__), "golden", "lognormal_table1.json")) as f:
+        return json.load(f)
+
+
+def test_lognormal_generator_is_a_popularity_sampler():
+    """sigma = 0 routes uniformly (expert loads within a few standard deviations of the mean);
+    K distinct experts per token; larger sigma concentrates load (rank peak/mean rises)."""
+    c = W.LOGNORMAL
+    peaks = []
+    for sg in c["sigmas"]:
+        topk, gates = W.lognormal_routing(c["R"], c["S"], c["E"], c["K"], sg)
+        O.validate_routing(np.array(topk), c["E"])
+        np.testing.assert_allclose(gates.sum(axis=-1), 1.0, atol=1e-5)
+        L = np.bincount(np.asarray(topk).ravel(), minlength=c["E"])
+        P = L.reshape(c["R"], -1).sum(axis=1)
+        peaks.append(P.max() / (c["S"] * c["K"]))
+        if sg == 0.0:
+            mean = c["R"] * c["S"] * c["K"] / c["E"]
+            assert np.abs(L - mean).max() <= 6 * np.sqrt(mean)
+    assert all(a < b for a, b in zip(peaks, peaks[1:]))
+
+
+@pytest.mark.parametrize("sigma", [0.0, 0.5, 1.0, 2.0, 5.0])
+def test_lognormal_plan_properties(sigma):
+    """Every rank gets exactly S*K rows at every skew; the copy count stays small (the post saw
+    7-9 with its generator); migration is at least its lower bound."""
+    c = W.LOGNORMAL
+    topk, _ = W.lognormal_routing(c["R"], c["S"], c["E"], c["K"], sigma)
+    topk = np.array(topk)
+    plan = O.make_plan(topk, c["E"], 4)
+    _plan_props(topk, plan, O.destinations(topk, plan))
+    st = O.stats_vector(plan)
+    P = np.bincount(topk.ravel(), minlength=c["E"]).reshape(c["R"], -1).sum(axis=1)
+    assert st[8] == P.max() and st[9] == P.min()      # baseline (home-pinned) rank loads
+    assert np.all(plan.cu[:, -1] == c["S"] * c["K"])  # after planning: exactly S*K everywhere
+    assert st[5] >= st[6]
+    assert 0 <= st[1] <= 12
+    table = {row[0]: row for row in _table1()["rows"]}
+    assert sigma in table     # the post's sweep points

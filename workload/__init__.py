@@ -33,7 +33,8 @@ import numpy as np
 
 __all__ = [
     "Config", "CONFIGS", "bf16_bits", "bf16_to_f32", "zipf_bias", "base_logits",
-    "route", "expert_load_maxvio", "tune_lambda", "routing_for", "hidden_rows",
+    "route", "expert_load_maxvio", "tune_lambda", "routing_for", "hidden_rows", "LOGNORMAL",
+    "lognormal_routing",
     "expert_weights_np", "expert_weights_torch", "grad_rows",
 ]
 
@@ -175,6 +176,32 @@ def routing_for(cfg: Config):
     topk, gates = route(base_logits(cfg.R, cfg.S, cfg.E, cfg.seed), zipf_bias(cfg.E, lam),
                         cfg.R, cfg.S, cfg.K)
     return topk, gates, lam
+
+
+# Lognormal expert popularity (the planner workload of the thakicloud.com post, "What we
+# measured", Table 1: 256 experts, 8 ranks, 2048 tokens per rank, top-8, skew set by a
+# lognormal sigma).  The post's generator is not available; this one samples each token's K
+# experts without replacement with probabilities proportional to w_e = exp(sigma * z_e),
+# z_e ~ N(0, 1) (Gumbel top-K: argsort of log w_e + Gumbel noise).  sigma = 0 is uniform
+# random routing, not the exactly balanced assignment the post's generator makes.
+LOGNORMAL = dict(R=8, E=256, S=2048, K=8, sigmas=(0.0, 0.5, 1.0, 2.0, 5.0))
+
+
+@functools.lru_cache(maxsize=8)
+def lognormal_routing(R: int, S: int, E: int, K: int, sigma: float, seed: int = 0):
+    """(topk int32 [R,S,K], gates float32 [R,S,K]); ties to the lower expert id."""
+    logw = (float(sigma) * _rng(seed, 5).standard_normal(E)).astype(np.float64)
+    u = _rng(seed, 6).random((R * S, E))
+    gumbel = -np.log(-np.log(np.clip(u, 1e-300, 1.0 - 1e-16)))
+    z = logw[None, :] + gumbel
+    order = np.argsort(-z, axis=1, kind="stable")[:, :K]
+    sel = np.take_along_axis(z, order, axis=1)
+    sel -= sel.max(axis=1, keepdims=True)
+    ex = np.exp(sel)
+    gates = (ex / ex.sum(axis=1, keepdims=True)).astype(np.float32)
+    topk = order.astype(np.int32).reshape(R, S, K)
+    topk.setflags(write=False)
+    return topk, gates.reshape(R, S, K)
 
 
 # ----------------------------------------------------------------------------
