@@ -376,16 +376,25 @@ __device__ __forceinline__ void pipeline64(f32x16_t (&acc)[4][WL<WN>::TN], char*
     block_sync();     // every wave is done with the buffers before the epilogue reuses them
 }
 
-// m-tile prefix of the groups (tile_pref[g] = 256-row tiles of groups before g), for the row kernels
+// m-tile prefix of the groups (tile_pref[g] = 256-row tiles of groups before g), for the row
+// kernels: one wave, 64 groups at a time, wave-wide inclusive scan with a running carry
 __global__ __launch_bounds__(64) void tile_prefix_kernel(PlanWs w) {
-    if (threadIdx.x != 0) return;
+    const int lane = threadIdx.x;
     const int ng = min(max(w.hdr[HDR_NGROUPS], 0), 2 * w.E);
     int run = 0;
-    for (int g = 0; g < ng; ++g) {
-        w.tile_pref[g] = run;
-        run += (group_rows(w.groups[g], w) + BM - 1) / BM;
+    for (int g0 = 0; g0 < ng; g0 += 64) {
+        const int g = g0 + lane;
+        const int v = g < ng ? (group_rows(w.groups[g], w) + BM - 1) / BM : 0;
+        int x = v;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(x, off);
+            if (lane >= off) x += y;
+        }
+        if (g < ng) w.tile_pref[g] = run + x - v;
+        run += __shfl(x, 63);
     }
-    w.tile_pref[ng] = run;
+    if (lane == 0) w.tile_pref[ng] = run;
 }
 
 // ---------------------------------------------------------------------------

@@ -31,19 +31,19 @@ SWEEP = (0.0, 0.5, 2.0, 4.0, 8.0)
 
 # timed call -> the one kernel it launches (name as in rocprofv3 kernel traces); the plan call
 # launches four small kernels and has no entry.  The weight-gradient calls also launch a
-# one-wave counter reset before their GEMM.
+# one-wave counter reset before their GEMM, the row GEMM calls a one-wave tile prefix.
 KERNEL_NAMES = {
     "prefetch": "moonep::prefetch_kernel",
-    "dispatch": "moonep::dispatch_kernel<false, false, 4>",
+    "dispatch": "moonep::dispatch_kernel<false, false, 4, false>",
     "gemm_gate_up": "moonep::gemm_rows_kernel<0, 0, 4>",
     "gemm_down": "moonep::gemm_rows_kernel<0, 1, 4>",
-    "combine": "moonep::combine_kernel<false, true, 8, 2>",
-    "dispatch_bwd": "moonep::dispatch_kernel<false, true, 4>",
+    "combine": "moonep::combine_kernel<false, true, 8, 2, false>",
+    "dispatch_bwd": "moonep::dispatch_kernel<false, true, 4, false>",
     "gemm_dact": "moonep::gemm_rows_kernel<1, 2, 4>",
     "gemm_dx": "moonep::gemm_rows_kernel<1, 1, 4>",
     "gemm_dw2": "moonep::gemm_dw_kernel<4, 2>",
     "gemm_dw13": "moonep::gemm_dw_kernel<4, 13>",
-    "combine_bwd": "moonep::combine_kernel<false, false, 8, 2>",
+    "combine_bwd": "moonep::combine_kernel<false, false, 8, 2, false>",
     "reduce_grad": "moonep::reduce_grad_kernel",
 }
 # sources each kernel is compiled from (a change to any of them voids its stored counters)
@@ -64,7 +64,7 @@ def parse():
     p.add_argument("--no-sweep", action="store_true", help="skip the maxvio sweep")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-tokens", type=int, default=4096, help="tokens per rank in the CPU sample")
-    p.add_argument("--cpu-groups", type=int, default=8, help="expert groups in the CPU FFN sample")
+    p.add_argument("--cpu-groups", type=int, default=32, help="expert groups in the CPU FFN sample")
     p.add_argument("--traffic-from", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "BENCH_JSON"),
                    help="no GPU work: reduce two rocprofv3 --pmc runs of this bench (FETCH_SIZE, then "
                         "WRITE_SIZE) and that run's JSON line to per-launch HBM bytes; writes "
