@@ -38,9 +38,27 @@ def _setup(cfg, B=None, training=False):
 
 @pytest.mark.parametrize("B", [4, 2, 0])
 def test_forward_mid(B):
-    cfg = MID.with_(B=B)
+    _forward_check(MID.with_(B=B))
+
+
+# tiles cut in every dimension: H and I not multiples of the 256-wide (128 for gate/up) tiles
+RAGGED = [dict(H=576, I=192), dict(H=320, I=448, K=3, S=300)]
+
+
+@pytest.mark.parametrize("over", RAGGED, ids=lambda o: "-".join(f"{k}{v}" for k, v in o.items()))
+def test_forward_ragged_tiles(over):
+    _forward_check(MID.with_(**over))
+
+
+@pytest.mark.parametrize("over", RAGGED, ids=lambda o: "-".join(f"{k}{v}" for k, v in o.items()))
+def test_backward_ragged_tiles(over):
+    _backward_check(MID.with_(**over))
+
+
+def _forward_check(cfg):
+    B = cfg.B
     topk, gates, xb, wb13, wb2, d, plan, dest, layer = _setup(cfg)
-    say("forward mid B", B, "replicas", len(plan.entries),
+    say("forward", cfg, "replicas", len(plan.entries),
         "fallback", sum(1 for e in plan.entries if e.w < cfg.E))
     out = layer.forward(bf16_from_bits(xb), i32(topk), f32(gates))
     torch.cuda.synchronize()
@@ -80,9 +98,13 @@ def test_forward_deterministic():
 
 @pytest.mark.parametrize("B", [4, 2, 0])
 def test_backward_mid(B):
-    cfg = MID.with_(B=B)
+    _backward_check(MID.with_(B=B))
+
+
+def _backward_check(cfg):
+    B = cfg.B
     topk, gates, xb, wb13, wb2, d, plan, dest, layer = _setup(cfg, training=True)
-    say("backward mid B", B)
+    say("backward", cfg)
     dout = W.grad_rows(cfg.R, cfg.S, cfg.H, cfg.seed, "bf16")
     layer.forward(bf16_from_bits(xb), i32(topk), f32(gates))
     dx = layer.backward(bf16_from_bits(dout), f32(gates))

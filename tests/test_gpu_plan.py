@@ -309,3 +309,21 @@ def test_plan_lognormal(sigma):
     say("plan lognormal sigma", sigma)
     plan, dest, (ws, cu, dd, st) = assert_plan_parity(d, np.array(topk))
     assert np.all(cu.cpu().numpy()[:, -1] == c["S"] * c["K"])
+
+
+def test_plan_dispatch_combine_max_dims():
+    """The largest dims the library accepts for the plan tables: 64 ranks, 1024 experts (16 per
+    rank), 64 slots, top-16."""
+    cfg = W.Config("max", R=64, E=1024, B=64, S=64, K=16, H=64, I=0, dtype="bf16", lam=1.0, seed=4)
+    topk, gates, _ = W.routing_for(cfg)
+    d = dims_of(cfg)
+    say("max dims")
+    plan, dest, (ws, cu, dd, st) = assert_plan_parity(d, topk)
+    x = W.hidden_rows(cfg.R, cfg.S, cfg.H, cfg.seed, "bf16")
+    recv = torch.empty((cfg.R * cfg.C, cfg.H), dtype=torch.bfloat16, device=DEV)
+    M.moonep_dispatch(d, dd, bf16_from_bits(x), None, recv)
+    out = torch.empty((cfg.R, cfg.S, cfg.H), dtype=torch.bfloat16, device=DEV)
+    M.moonep_combine(d, dd, recv, f32(gates), out)
+    torch.cuda.synchronize()
+    assert bits_of(recv).tobytes() == O.dispatch(dest, x).tobytes()
+    assert max_row_rel(f64_of(out), O.combine(dest, O.dispatch(dest, x), gates)) <= 1e-2
