@@ -28,6 +28,8 @@
 //
 // Ties always go to the lower rank / expert id; integer arithmetic only, so the
 // result is bit-identical from run to run.
+#include <climits>
+
 #include "common.h"
 
 namespace moonep {
@@ -87,21 +89,13 @@ __global__ __launch_bounds__(256) void plan_scan(PlanWs w) {
     if (lane == 0) w.L[e] = run;
 }
 
-__device__ __forceinline__ long long wave_min_ll(long long v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const long long y = __shfl_xor(v, o, 64);
-        v = y < v ? y : v;
-    }
-    return v;
-}
-__device__ __forceinline__ long long wave_max_ll(long long v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const long long y = __shfl_xor(v, o, 64);
-        v = y > v ? y : v;
-    }
-    return v;
+// wave-wide min / max of a 32-bit value (DPP-based reductions of the device library)
+extern "C" __device__ int __ockl_wfred_min_i32(int);
+extern "C" __device__ int __ockl_wfred_max_i32(int);
+
+// lowest lane whose flag is set (flags wave-uniformly nonzero)
+__device__ __forceinline__ int first_lane(bool f) {
+    return __builtin_ctzll(__ballot(f));
 }
 
 struct DecideShared {
@@ -110,9 +104,9 @@ struct DecideShared {
     int ent[kMaxE][5];     // e, q, a, j, w
     int P[kMaxR], X[kMaxR];
     int don[kMaxR], rec[kMaxR];
-    int nd, nr, nent, status, ngroups;
+    int nd, nr, nent, status, ngroups, nred;
     int rank_nent[kMaxR];
-    int trows[kMaxE + kMaxR * kMaxB];   // rows of each dW target
+    alignas(16) int trows[kMaxE + kMaxR * kMaxB];   // rows of each dW target (-1 padding)
 };
 
 __global__ __launch_bounds__(256) void plan_decide(PlanWs w, uint32_t flags, int32_t* __restrict__ cu,
@@ -125,6 +119,7 @@ __global__ __launch_bounds__(256) void plan_decide(PlanWs w, uint32_t flags, int
         sh.status = 0;
         sh.nent = 0;
         sh.ngroups = 0;
+        sh.nred = 0;
     }
     __syncthreads();
     int st = 0;
@@ -176,16 +171,15 @@ __global__ __launch_bounds__(256) void plan_decide(PlanWs w, uint32_t flags, int
             int av = lane < G ? sh.avail[e] : 0;
             while (amt > 0 && !fail) {
                 // best fit: fewest remaining rows that still cover amt (ties: lower id)
-                long long k1 = (lane < G && av >= amt) ? (((long long)av << 8) | lane) : LLONG_MAX;
-                k1 = wave_min_ll(k1);
+                const bool cover = lane < G && av >= amt;
                 int pick;
-                if (k1 != LLONG_MAX) {
-                    pick = (int)(k1 & 0xff);
+                if (__ballot(cover)) {
+                    const int m = __ockl_wfred_min_i32(cover ? av : INT_MAX);
+                    pick = first_lane(cover && av == m);
                 } else {
                     // otherwise the most remaining rows (ties: lower id), all of them
-                    long long k2 = lane < G ? (((long long)av << 8) | (255 - lane)) : -1;
-                    k2 = wave_max_ll(k2);
-                    pick = 255 - (int)(k2 & 0xff);
+                    const int m = __ockl_wfred_max_i32(lane < G ? av : -1);
+                    pick = first_lane(lane < G && av == m);
                 }
                 const int pav = __shfl(av, pick, 64);
                 const int a = pav < amt ? pav : amt;
@@ -313,6 +307,7 @@ __global__ __launch_bounds__(256) void plan_decide(PlanWs w, uint32_t flags, int
             }
             w.red_n[e] = nred;
             w.fb_n[e] = nfb;
+            if (nred > 0) atomicAdd(&sh.nred, 1);
             w.home_seg[e] = Segment{h * C + cu[h * ncu + e], sh.avail[e]};
         } else {
             w.red_n[e] = 0;
@@ -368,6 +363,8 @@ __global__ __launch_bounds__(256) void plan_decide(PlanWs w, uint32_t flags, int
     // dW targets (home experts with their fallback replicas, then slots) by rows, descending:
     // the weight-gradient GEMM hands out the largest first (longest-processing-time order)
     const int ntarget = E + R * B;
+    const int n4 = (ntarget + 3) / 4;
+    for (int t = ntarget + tid; t < n4 * 4; t += 256) sh.trows[t] = -1;
     for (int t = tid; t < ntarget; t += 256) {
         int rows = 0;
         if (ok) {
@@ -383,12 +380,19 @@ __global__ __launch_bounds__(256) void plan_decide(PlanWs w, uint32_t flags, int
         sh.trows[t] = rows;
     }
     __syncthreads();
+    // rank = targets with more rows, or as many and a lower index (four per broadcast LDS read)
     for (int t = tid; t < ntarget; t += 256) {
         const int r = sh.trows[t];
         int rank = 0;
-        for (int u = 0; u < ntarget; ++u) {
-            const int v = sh.trows[u];
-            rank += (v > r) || (v == r && u < t);
+        const int4* tv = reinterpret_cast<const int4*>(sh.trows);
+#pragma unroll 4
+        for (int u4 = 0; u4 < n4; ++u4) {
+            const int4 v = tv[u4];
+            const int u = u4 * 4;
+            rank += (v.x > r) || (v.x == r && u < t);
+            rank += (v.y > r) || (v.y == r && u + 1 < t);
+            rank += (v.z > r) || (v.z == r && u + 2 < t);
+            rank += (v.w > r) || (v.w == r && u + 3 < t);
         }
         w.dw_order[rank] = t;
     }
@@ -414,8 +418,7 @@ __global__ __launch_bounds__(256) void plan_decide(PlanWs w, uint32_t flags, int
         for (int e = 0; e < E; ++e) maxl = sh.L[e] > maxl ? sh.L[e] : maxl;
         int status = sh.status;
         if (ok && nfb > 0 && (flags & MOONEP_TRAINING)) status |= MOONEP_ST_TRAIN_FALLBACK;
-        int nred = 0;
-        for (int e = 0; e < E; ++e) nred += ok && w.red_n[e] > 0;
+        const int nred = ok ? sh.nred : 0;
         const int v[MOONEP_NSTATS] = {status, nent, nslot, nfb, fbrows, migr, bound, maxl, maxp, minp,
                                       nd, nr, maxper, total, 0, 0};
         for (int i = 0; i < MOONEP_NSTATS; ++i) stats[i] = v[i];
