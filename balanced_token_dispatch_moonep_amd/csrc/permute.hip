@@ -13,46 +13,69 @@
 // Both are HBM-bound row copies.  One wave owns one token: each lane moves 16-byte
 // vectors, so every load or store instruction of the wave covers 1 KiB of one row
 // (fully coalesced).  The token's source row is read once and written K times
-// (dispatch); K rows are gathered with all loads of a vector batch in flight before
-// the float32 accumulation (combine).
+// (dispatch); the K rows of a token are gathered one after another, a chunk of the row
+// at a time, into float32 accumulators (combine).
 #include "common.h"
 
 namespace moonep {
 
 constexpr int kWavesPerBlock = 4;
+// Vectors (16 bytes) per lane that one batch of a row moves; chosen by measurement on MI355X at
+// H = 7168 (896 vectors per bf16 row).
+#ifndef MOONEP_DISPATCH_VB
+#define MOONEP_DISPATCH_VB 2
+#endif
+#ifndef MOONEP_DISPATCH_SCALED_VB
+#define MOONEP_DISPATCH_SCALED_VB 2
+#endif
+#ifndef MOONEP_COMBINE_VB
+#define MOONEP_COMBINE_VB 7
+#endif
 
 template <bool F32, bool SCALE>
 __device__ __forceinline__ uint4 scale_vec(uint4 v, float g) {
-    if (!SCALE) return v;
-    uint4 o;
-    if (F32) {
-        o.x = __float_as_uint(__uint_as_float(v.x) * g);
-        o.y = __float_as_uint(__uint_as_float(v.y) * g);
-        o.z = __float_as_uint(__uint_as_float(v.z) * g);
-        o.w = __float_as_uint(__uint_as_float(v.w) * g);
+    if constexpr (!SCALE) {
+        return v;
+    } else if constexpr (F32) {
+        return make_uint4(__float_as_uint(__uint_as_float(v.x) * g), __float_as_uint(__uint_as_float(v.y) * g),
+                          __float_as_uint(__uint_as_float(v.z) * g), __float_as_uint(__uint_as_float(v.w) * g));
     } else {
-        o.x = pack_bf16(bf16_lo(v.x) * g, bf16_hi(v.x) * g);
-        o.y = pack_bf16(bf16_lo(v.y) * g, bf16_hi(v.y) * g);
-        o.z = pack_bf16(bf16_lo(v.z) * g, bf16_hi(v.z) * g);
-        o.w = pack_bf16(bf16_lo(v.w) * g, bf16_hi(v.w) * g);
+        return make_uint4(pack_bf16(bf16_lo(v.x) * g, bf16_hi(v.x) * g), pack_bf16(bf16_lo(v.y) * g, bf16_hi(v.y) * g),
+                          pack_bf16(bf16_lo(v.z) * g, bf16_hi(v.z) * g), pack_bf16(bf16_lo(v.w) * g, bf16_hi(v.w) * g));
     }
-    return o;
 }
 
 // recv[dest[p]] = scale(src[token(p)]); one wave per token, 16-byte vectors per lane.
+// A batch of VB vectors per lane of the source row is read once (non-temporal) and written to
+// the token's K destination rows with ordinary stores (measured faster than non-temporal ones
+// for this scatter of 1 KiB wave segments).  KT > 0 (the scaled form at K = 8): compile-time
+// K, and the token's K destinations and scales are read once, before its row, which keeps the
+// scale loads out of the store loop; the unscaled form reads its destinations in the loop
+// (measured faster).
 // IDENT: dest[p] = p (rows land in arrival order: the first copy of the staged baseline).
-template <bool F32, bool SCALE, int VB, bool IDENT = false>
+template <bool F32, bool SCALE, int KT, int VB, bool IDENT = false>
 __global__ __launch_bounds__(256) void dispatch_kernel(const int32_t* __restrict__ dest,
                                                        const uint4* __restrict__ src,
                                                        const float* __restrict__ scale,
-                                                       uint4* __restrict__ recv, int ntok, int K,
+                                                       uint4* __restrict__ recv, int ntok, int Krt,
                                                        int rowvec, long long nrows) {
+    constexpr int KA = KT > 0 ? KT : 1;
+    const int K = KT > 0 ? KT : Krt;
     const int tok = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (tok >= ntok) return;
     const int32_t* dp = dest + (size_t)tok * K;
     const float* gp = SCALE ? scale + (size_t)tok * K : nullptr;
     const uint4* s = src + (size_t)tok * rowvec;
+    int dk[KA];
+    float gk[KA];
+    if constexpr (KT > 0) {
+#pragma unroll
+        for (int k = 0; k < KT; ++k) {
+            dk[k] = IDENT ? tok * KT + k : dp[k];
+            gk[k] = SCALE ? gp[k] : 1.0f;
+        }
+    }
     for (int v0 = 0; v0 < rowvec; v0 += 64 * VB) {
         uint4 x[VB];
 #pragma unroll
@@ -60,23 +83,27 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const int32_t* __restrict
             const int v = v0 + u * 64 + lane;
             if (v < rowvec) x[u] = ld_nt(s + v);
         }
-        for (int k = 0; k < K; ++k) {
-            const int d = IDENT ? tok * K + k : dp[k];
-            if ((unsigned long long)(long long)d >= (unsigned long long)nrows) continue;
-            const float g = SCALE ? gp[k] : 1.0f;
+        auto put = [&](int d, float g) {
+            if ((unsigned long long)(long long)d >= (unsigned long long)nrows) return;
             uint4* o = recv + (size_t)d * rowvec;
 #pragma unroll
             for (int u = 0; u < VB; ++u) {
                 const int v = v0 + u * 64 + lane;
-                if (v < rowvec) st_nt(scale_vec<F32, SCALE>(x[u], g), o + v);
+                if (v < rowvec) o[v] = scale_vec<F32, SCALE>(x[u], g);
             }
+        };
+        if constexpr (KT > 0) {
+#pragma unroll
+            for (int k = 0; k < KT; ++k) put(dk[k], gk[k]);
+        } else {
+            for (int k = 0; k < K; ++k) put(IDENT ? tok * K + k : dp[k], SCALE ? gp[k] : 1.0f);
         }
     }
 }
 
 template <bool F32>
 __device__ __forceinline__ void acc_vec(float* a, uint4 v, float g) {
-    if (F32) {
+    if constexpr (F32) {
         a[0] += g * __uint_as_float(v.x);
         a[1] += g * __uint_as_float(v.y);
         a[2] += g * __uint_as_float(v.z);
@@ -94,16 +121,17 @@ __device__ __forceinline__ void acc_vec(float* a, uint4 v, float g) {
 }
 
 // out[token] = sum_k g_k * y[dest[p_k]] (k order, float32); one wave per token.
-// KT > 0: compile-time K (all K loads of a vector batch issued before accumulating).
+// The output row is produced in chunks of VB vectors per lane; for a chunk the K source rows
+// are read one after another, VB KiB of one row at a time (measured faster than keeping all K
+// rows' loads in flight, which spreads each wave over K places of HBM at once).
 // IDENT: dest[p] = p (rows read in arrival order: the reduction of the staged baseline).
-template <bool F32, bool GATES, int KT, int VB, bool IDENT = false>
+template <bool F32, bool GATES, int VB, bool IDENT = false>
 __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ dest,
                                                       const uint4* __restrict__ y,
                                                       const float* __restrict__ gates,
-                                                      uint4* __restrict__ out, int ntok, int Krt,
+                                                      uint4* __restrict__ out, int ntok, int K,
                                                       int rowvec, long long nrows) {
     constexpr int NE = F32 ? 4 : 8;
-    const int K = KT > 0 ? KT : Krt;
     const int tok = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (tok >= ntok) return;
@@ -116,36 +144,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
         for (int u = 0; u < VB; ++u)
 #pragma unroll
             for (int i = 0; i < NE; ++i) acc[u][i] = 0.0f;
-        if (KT > 0) {
-            uint4 x[KT > 0 ? KT : 1][VB];
+#pragma unroll 1
+        for (int k = 0; k < K; ++k) {
+            const int d = IDENT ? tok * K + k : dp[k];
+            if ((unsigned long long)(long long)d >= (unsigned long long)nrows) continue;
+            const float g = GATES ? gp[k] : 1.0f;
+            const uint4* yr = y + (size_t)d * rowvec;
 #pragma unroll
-            for (int k = 0; k < (KT > 0 ? KT : 1); ++k) {
-                const int d = IDENT ? tok * K + k : dp[k];
-                const bool ok = (unsigned long long)(long long)d < (unsigned long long)nrows;
-                const uint4* yr = y + (size_t)(ok ? d : 0) * rowvec;
-#pragma unroll
-                for (int u = 0; u < VB; ++u) {
-                    const int v = v0 + u * 64 + lane;
-                    x[k][u] = (ok && v < rowvec) ? ld_nt(yr + v) : make_uint4(0, 0, 0, 0);
-                }
-            }
-#pragma unroll
-            for (int k = 0; k < (KT > 0 ? KT : 1); ++k) {
-                const float g = GATES ? gp[k] : 1.0f;
-#pragma unroll
-                for (int u = 0; u < VB; ++u) acc_vec<F32>(acc[u], x[k][u], g);
-            }
-        } else {
-            for (int k = 0; k < K; ++k) {
-                const int d = IDENT ? tok * K + k : dp[k];
-                if ((unsigned long long)(long long)d >= (unsigned long long)nrows) continue;
-                const float g = GATES ? gp[k] : 1.0f;
-                const uint4* yr = y + (size_t)d * rowvec;
-#pragma unroll
-                for (int u = 0; u < VB; ++u) {
-                    const int v = v0 + u * 64 + lane;
-                    if (v < rowvec) acc_vec<F32>(acc[u], ld_nt(yr + v), g);
-                }
+            for (int u = 0; u < VB; ++u) {
+                const int v = v0 + u * 64 + lane;
+                if (v < rowvec) acc_vec<F32>(acc[u], ld_nt(yr + v), g);
             }
         }
 #pragma unroll
@@ -153,41 +161,35 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
             const int v = v0 + u * 64 + lane;
             if (v >= rowvec) continue;
             uint4 r;
-            if (F32) {
-                r.x = __float_as_uint(acc[u][0]);
-                r.y = __float_as_uint(acc[u][1]);
-                r.z = __float_as_uint(acc[u][2]);
-                r.w = __float_as_uint(acc[u][3]);
+            if constexpr (F32) {
+                r = make_uint4(__float_as_uint(acc[u][0]), __float_as_uint(acc[u][1]), __float_as_uint(acc[u][2]),
+                               __float_as_uint(acc[u][3]));
             } else {
-                r.x = pack_bf16(acc[u][0], acc[u][1]);
-                r.y = pack_bf16(acc[u][2], acc[u][3]);
-                r.z = pack_bf16(acc[u][4], acc[u][5]);
-                r.w = pack_bf16(acc[u][6], acc[u][7]);
+                r = make_uint4(pack_bf16(acc[u][0], acc[u][1]), pack_bf16(acc[u][2], acc[u][3]),
+                               pack_bf16(acc[u][4], acc[u][5]), pack_bf16(acc[u][6], acc[u][7]));
             }
             st_nt(r, o + v);
         }
     }
 }
 
+template <bool F32, bool SCALE, bool IDENT = false>
+static void launch_dispatch(int K, dim3 grid, hipStream_t s, const int32_t* dest, const uint4* src,
+                            const float* scale, uint4* recv, int ntok, int rowvec, long long nrows) {
+    constexpr int VB = SCALE ? MOONEP_DISPATCH_SCALED_VB : MOONEP_DISPATCH_VB;
+    if constexpr (SCALE) {
+        if (K == 8) {
+            hipLaunchKernelGGL((dispatch_kernel<F32, SCALE, 8, VB, IDENT>), grid, dim3(256), 0, s, dest, src, scale, recv, ntok, K, rowvec, nrows);
+            return;
+        }
+    }
+    hipLaunchKernelGGL((dispatch_kernel<F32, SCALE, 0, VB, IDENT>), grid, dim3(256), 0, s, dest, src, scale, recv, ntok, K, rowvec, nrows);
+}
+
 template <bool F32, bool GATES, bool IDENT = false>
 static void launch_combine(int K, dim3 grid, hipStream_t s, const int32_t* dest, const uint4* y,
                            const float* gates, uint4* out, int ntok, int rowvec, long long nrows) {
-    switch (K) {
-        case 8:
-            hipLaunchKernelGGL((combine_kernel<F32, GATES, 8, 2, IDENT>), grid, dim3(256), 0, s, dest, y, gates, out, ntok, K, rowvec, nrows);
-            break;
-        case 4:
-            hipLaunchKernelGGL((combine_kernel<F32, GATES, 4, 4, IDENT>), grid, dim3(256), 0, s, dest, y, gates, out, ntok, K, rowvec, nrows);
-            break;
-        case 2:
-            hipLaunchKernelGGL((combine_kernel<F32, GATES, 2, 4, IDENT>), grid, dim3(256), 0, s, dest, y, gates, out, ntok, K, rowvec, nrows);
-            break;
-        case 1:
-            hipLaunchKernelGGL((combine_kernel<F32, GATES, 1, 4, IDENT>), grid, dim3(256), 0, s, dest, y, gates, out, ntok, K, rowvec, nrows);
-            break;
-        default:
-            hipLaunchKernelGGL((combine_kernel<F32, GATES, 0, 2, IDENT>), grid, dim3(256), 0, s, dest, y, gates, out, ntok, K, rowvec, nrows);
-    }
+    hipLaunchKernelGGL((combine_kernel<F32, GATES, MOONEP_COMBINE_VB, IDENT>), grid, dim3(256), 0, s, dest, y, gates, out, ntok, K, rowvec, nrows);
 }
 
 // The sort-copy of the staged baseline, one wave per row p, 16-byte vectors per lane:
@@ -239,15 +241,11 @@ extern "C" int moonep_dispatch(const moonep_dims_t* dims, const int32_t* dest, c
     const uint4* sv = static_cast<const uint4*>(src);
     uint4* rv = static_cast<uint4*>(recv);
     if (f32) {
-        if (row_scale)
-            hipLaunchKernelGGL((dispatch_kernel<true, true, 4>), grid, dim3(256), 0, s, dest, sv, row_scale, rv, ntok, dims->K, rowvec, nrows);
-        else
-            hipLaunchKernelGGL((dispatch_kernel<true, false, 4>), grid, dim3(256), 0, s, dest, sv, row_scale, rv, ntok, dims->K, rowvec, nrows);
+        if (row_scale) launch_dispatch<true, true>(dims->K, grid, s, dest, sv, row_scale, rv, ntok, rowvec, nrows);
+        else launch_dispatch<true, false>(dims->K, grid, s, dest, sv, row_scale, rv, ntok, rowvec, nrows);
     } else {
-        if (row_scale)
-            hipLaunchKernelGGL((dispatch_kernel<false, true, 4>), grid, dim3(256), 0, s, dest, sv, row_scale, rv, ntok, dims->K, rowvec, nrows);
-        else
-            hipLaunchKernelGGL((dispatch_kernel<false, false, 4>), grid, dim3(256), 0, s, dest, sv, row_scale, rv, ntok, dims->K, rowvec, nrows);
+        if (row_scale) launch_dispatch<false, true>(dims->K, grid, s, dest, sv, row_scale, rv, ntok, rowvec, nrows);
+        else launch_dispatch<false, false>(dims->K, grid, s, dest, sv, row_scale, rv, ntok, rowvec, nrows);
     }
     MOONEP_LAUNCH_CHECK();
     return MOONEP_OK;
@@ -300,15 +298,11 @@ extern "C" int moonep_dispatch_staged(const moonep_dims_t* dims, const int32_t* 
     uint4* tv = static_cast<uint4*>(stage);
     // 1. arrival order: stage[(r, s, k)] = scale(src[r, s])
     if (f32) {
-        if (row_scale)
-            hipLaunchKernelGGL((dispatch_kernel<true, true, 4, true>), grid, dim3(256), 0, s, dest, sv, row_scale, tv, ntok, dims->K, rowvec, nrows);
-        else
-            hipLaunchKernelGGL((dispatch_kernel<true, false, 4, true>), grid, dim3(256), 0, s, dest, sv, row_scale, tv, ntok, dims->K, rowvec, nrows);
+        if (row_scale) launch_dispatch<true, true, true>(dims->K, grid, s, dest, sv, row_scale, tv, ntok, rowvec, nrows);
+        else launch_dispatch<true, false, true>(dims->K, grid, s, dest, sv, row_scale, tv, ntok, rowvec, nrows);
     } else {
-        if (row_scale)
-            hipLaunchKernelGGL((dispatch_kernel<false, true, 4, true>), grid, dim3(256), 0, s, dest, sv, row_scale, tv, ntok, dims->K, rowvec, nrows);
-        else
-            hipLaunchKernelGGL((dispatch_kernel<false, false, 4, true>), grid, dim3(256), 0, s, dest, sv, row_scale, tv, ntok, dims->K, rowvec, nrows);
+        if (row_scale) launch_dispatch<false, true, true>(dims->K, grid, s, dest, sv, row_scale, tv, ntok, rowvec, nrows);
+        else launch_dispatch<false, false, true>(dims->K, grid, s, dest, sv, row_scale, tv, ntok, rowvec, nrows);
     }
     MOONEP_LAUNCH_CHECK();
     // 2. the sort into expert order: recv[dest[p]] = stage[p]

@@ -47,6 +47,10 @@ __global__ __launch_bounds__(256) void prefetch_kernel(PlanWs w, const uint4* __
     }
 }
 
+#ifndef MOONEP_REDUCE_U
+#define MOONEP_REDUCE_U 4
+#endif
+
 __global__ __launch_bounds__(256) void reduce_grad_kernel(PlanWs w, float4* __restrict__ d13,
                                                           float4* __restrict__ d2,
                                                           float4* __restrict__ r13,
@@ -63,20 +67,35 @@ __global__ __launch_bounds__(256) void reduce_grad_kernel(PlanWs w, float4* __re
     const long long per = (n + kCopyBlocks - 1) / kCopyBlocks;
     const long long lo = per * blockIdx.x;
     const long long hi = lo + per < n ? lo + per : n;
-    for (long long i = lo + threadIdx.x; i < hi; i += 256) {
-        float4 a = home[i];
+    // U vectors per thread per pass, all loads of a replica issued before its adds (replicas are
+    // added in creation order, so every element sees the same sequence of float32 additions)
+    constexpr int U = MOONEP_REDUCE_U;
+    for (long long i0 = lo + threadIdx.x; i0 < hi; i0 += 256 * U) {
+        float4 a[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (i0 + u * 256 < hi) a[u] = home[i0 + u * 256];
         for (int r = 0; r < nred; ++r) {
             const int sl = slots[r];
             if (sl < 0 || sl >= w.R * w.B) continue;
-            float4* rb = red + (size_t)sl * n + i;
-            const float4 v = ld_nt(rb);
-            a.x += v.x;
-            a.y += v.y;
-            a.z += v.z;
-            a.w += v.w;
-            st_nt(make_float4(0.f, 0.f, 0.f, 0.f), rb);
+            float4* rb = red + (size_t)sl * n + i0;
+            float4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (i0 + u * 256 < hi) v[u] = ld_nt(rb + u * 256);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (i0 + u * 256 >= hi) continue;
+                a[u].x += v[u].x;
+                a[u].y += v[u].y;
+                a[u].z += v[u].z;
+                a[u].w += v[u].w;
+                st_nt(make_float4(0.f, 0.f, 0.f, 0.f), rb + u * 256);
+            }
         }
-        home[i] = a;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (i0 + u * 256 < hi) home[i0 + u * 256] = a[u];
     }
 }
 
