@@ -126,6 +126,12 @@ __device__ __forceinline__ void dma16(const uint16_t* g, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
                  : "memory", "m0");
 }
+// The same copy from a wave-uniform base (scalar registers) plus a per-lane 32-bit byte offset:
+// the address arithmetic stays on the scalar unit (one base per stage), not on 64-bit vector adds.
+__device__ __forceinline__ void dma16s(const uint16_t* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds)
+                 : "memory", "m0");
+}
 #pragma clang diagnostic pop
 // LDS byte address of a pointer into dynamic shared memory
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -594,21 +600,21 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_rows_kernel(GemmArgs a) {
         const uint16_t* W = gr.wsel >= 0 ? a.Bhome + (size_t)gr.wsel * a.bstride
                                          : a.Bslot + (size_t)(-1 - gr.wsel) * a.bstride;
 
-        // per-lane sources of this wave's DMA loads (2*PARTS per operand and stage), as element
-        // offsets from the operand base; rows and columns outside the tile clamp to the last valid
-        // one (their products only reach outputs the epilogue does not store)
+        // per-lane sources of this wave's DMA loads (2*PARTS per operand and stage), as byte
+        // offsets from the stage's operand base; rows and columns outside the tile clamp to the
+        // last valid one (their products only reach outputs the epilogue does not store)
         constexpr int P2 = 2 * L::PARTS;
-        int ao[P2], bo[P2];
+        uint32_t ao[P2], bo[P2];
 #pragma unroll
         for (int i = 0; i < P2; ++i) {
             const int p = (wave * P2 + i) * 64 + lane;
             {   // A: k-contiguous activations [rows, K]
                 const int r = p >> 3, c = (p & 7) ^ ((r >> 1) & 7);
-                ao[i] = (row0 + min(r, mvalid - 1)) * a.lda + c * 8;
+                ao[i] = 2u * (uint32_t)((row0 + min(r, mvalid - 1)) * a.lda + c * 8);
             }
             if (MODE == ROWS_BK) {   // weights [N, K]
                 const int r = p >> 3, c = (p & 7) ^ ((r >> 1) & 7);
-                bo[i] = min(nt * BN + r, a.N - 1) * a.ldb + c * 8;
+                bo[i] = 2u * (uint32_t)(min(nt * BN + r, a.N - 1) * a.ldb + c * 8);
             } else {                 // weights [K, N]
                 const int k = p >> 5, c = (p & 31) ^ ((k & 3) << 2);
                 int col;
@@ -618,7 +624,7 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_rows_kernel(GemmArgs a) {
                 } else {
                     col = min(nt * BN + c * 8, a.N - 8);
                 }
-                bo[i] = k * a.ldb + col;
+                bo[i] = 2u * (uint32_t)(k * a.ldb + col);
             }
         }
         const int bstep = MODE == ROWS_BK ? BK2 : BK2 * a.ldb;
@@ -629,8 +635,15 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_rows_kernel(GemmArgs a) {
         pipeline64<MODE == ROWS_BK, EPI, WN, EPI == EPI_STORE>(acc, smem, a.K / BK2, wm, wn, lane,
                                              [&](int op, int s, int buf, int i) {
             const uint32_t l = lds_wave + buf * OP2_BYTES + i * 1024;
-            if (op == 0) dma16(A0 + (ao[i] + s * BK2), l);
-            else dma16(W + (bo[i] + s * bstep), l);
+            // scalar stage base + per-lane offset; the dX kernel (k-contiguous weights, plain
+            // store) measured 4% faster with per-lane 64-bit addresses, so it keeps them
+            if constexpr (MODE == ROWS_BK && EPI == EPI_STORE) {
+                if (op == 0) dma16(A0 + (ao[i] / 2 + s * BK2), l);
+                else dma16(W + (bo[i] / 2 + s * bstep), l);
+            } else {
+                if (op == 0) dma16s(A0 + s * BK2, ao[i], l);
+                else dma16s(W + (size_t)s * bstep, bo[i], l);
+            }
         });
         epi_rows_quarter<EPI, WN, 0>(a, acc, ep, wm, wn, lane, nt, row0, mvalid);
         epi_rows_quarter<EPI, WN, 1>(a, acc, ep, wm, wn, lane, nt, row0, mvalid);
@@ -701,29 +714,35 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_dw_kernel(GemmArgs a) {
         f32x16_t acc[4][L::TN];
         zero_acc<L::TN>(acc);
         if (nst > 0) {
-            int kk_i[L::PARTS], ac[L::PARTS], bc[L::PARTS], zc[L::PARTS];
-            bool aok[L::PARTS], bok[L::PARTS];
+            // per-lane source of each DMA load: k-row kk of the step and a 16-byte column chunk,
+            // as byte offsets from the step's first row; columns outside the tile clamp to the last
+            // valid chunk (their products only reach outputs the epilogue does not store)
+            uint32_t ao[L::PARTS], bo[L::PARTS];
 #pragma unroll
             for (int i = 0; i < L::PARTS; ++i) {
                 const int p = (wave * L::PARTS + i) * 64 + lane;
                 const int k = p >> 5, c = (p & 31) ^ ((k & 3) << 2);
-                kk_i[i] = k;
-                zc[i] = c * 8;
-                ac[i] = m0 + c * 8;
-                bc[i] = n0 + c * 8;
-                aok[i] = ac[i] < a.M;
-                bok[i] = bc[i] < a.N;
+                ao[i] = 2u * (uint32_t)(k * a.lda + min(m0 + c * 8, a.M - 8));
+                bo[i] = 2u * (uint32_t)(k * a.ldb + min(n0 + c * 8, a.N - 8));
             }
-            // issue cursor over the segments (runs NSTAGE-1 steps ahead of the compute)
+            // issue cursor over the segments (runs NSTAGE-1 steps ahead of the compute); rows past
+            // a segment's end, in its last step, load zeros
             int iseg = 0, ikoff = 0;
             Segment icur = s_seg[0];
             pipeline<false, false, EPI_ACC_F32, WN>(acc, smem, nst, wm, wn, lane, [&](int, int buf, int i) {
                 const uint32_t l = lds_wave + buf * STAGE_BYTES + i * 1024;
-                const int kr = ikoff + kk_i[i];
-                const bool v = kr < icur.rows;
-                const size_t row = (size_t)(icur.row0 + kr);
-                dma16(v && aok[i] ? a.A + row * a.lda + ac[i] : w.zeros + zc[i], l);
-                dma16(v && bok[i] ? a.B + row * a.ldb + bc[i] : w.zeros + zc[i], l + OP_BYTES);
+                const int row = __builtin_amdgcn_readfirstlane(icur.row0 + ikoff);
+                const int left = __builtin_amdgcn_readfirstlane(icur.rows - ikoff);
+                const uint16_t* ga = a.A + (size_t)row * a.lda;
+                const uint16_t* gb = a.B + (size_t)row * a.ldb;
+                if (left >= BK) {
+                    dma16s(ga, ao[i], l);
+                    dma16s(gb, bo[i], l + OP_BYTES);
+                } else {    // k-row of this lane's load: ((wave * PARTS + i) * 64 + lane) / 32
+                    const bool v = (wave * L::PARTS + i) * 2 + (lane >> 5) < left;
+                    dma16(v ? ga + ao[i] / 2 : w.zeros, l);
+                    dma16(v ? gb + bo[i] / 2 : w.zeros, l + OP_BYTES);
+                }
                 if (i == L::PARTS - 1) {    // step issued: advance the cursor
                     ikoff += BK;
                     if (ikoff >= icur.rows) {
