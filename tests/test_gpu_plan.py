@@ -167,17 +167,26 @@ def test_dispatch_full_size(maxvio):
         assert torch.equal(recv[lo:hi].view(torch.int16), xs[src_tok[lo:hi]].view(torch.int16))
 
 
-def test_dispatch_row_scale():
-    cfg = W.CONFIGS["skew"].with_(S=128, H=512, maxvio=4.0)
+@pytest.mark.parametrize("name,over", [
+    ("skew", {"S": 128, "H": 512, "maxvio": 4.0}),      # K = 8: scales loaded before the row
+    ("balanced", {"S": 64, "H": 264, "K": 3}),          # K read at run time, ragged last batch
+    ("tiny", {}),                                       # float32 rows
+])
+def test_dispatch_row_scale(name, over):
+    cfg = W.CONFIGS[name].with_(**over)
     topk, gates, x, d, plan, dest, dd = _layer_inputs(cfg)
-    dout = W.grad_rows(cfg.R, cfg.S, cfg.H, 1, "bf16")
-    recv = torch.empty((cfg.R * cfg.C, cfg.H), dtype=torch.bfloat16, device=DEV)
-    M.moonep_dispatch(d, dd, bf16_from_bits(dout), f32(gates), recv)
+    say("dispatch row scale", name, over)
+    dout = W.grad_rows(cfg.R, cfg.S, cfg.H, 1, cfg.dtype)
+    recv = torch.empty((cfg.R * cfg.C, cfg.H), dtype=torch.float32 if cfg.dtype == "f32" else torch.bfloat16,
+                       device=DEV)
+    M.moonep_dispatch(d, dd, rows_tensor(dout), f32(gates), recv)
     torch.cuda.synchronize()
     ref = O.dispatch(dest, dout, row_scale=gates)
     got = f64_of(recv)
-    # one float32 product rounded once to bf16: within half a bf16 ulp (2^-9 relative)
-    assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-30)
+    # one float32 product rounded once to the row type: within half an ulp of it
+    # (bf16: 2^-9 relative, float32: 2^-24 relative)
+    tol = 2.0 ** -23 if cfg.dtype == "f32" else 2.0 ** -8
+    assert np.all(np.abs(got - ref) <= np.abs(ref) * tol + 1e-30)
 
 
 # ----------------------------------------------------------------------------
