@@ -45,6 +45,10 @@ constexpr int BM = 256, BN = 256, BK = 32, NSTAGE = 4;
 constexpr int OP_BYTES = 256 * BK * 2;             // one operand tile of one stage: 16 KiB
 constexpr int STAGE_BYTES = 2 * OP_BYTES;
 constexpr int GEMM_SMEM = NSTAGE * STAGE_BYTES;    // 128 KiB
+// weight-gradient kernel: float4 stores per wave and tile (8 waves of 128x64), and the start of
+// its epilogue staging (ring buffer 3 onwards, clear of the next tile's first three steps)
+constexpr int DW_STORES = 32;
+constexpr int DW_STG = 3 * STAGE_BYTES;
 // Row kernels: K step 64, so every k-contiguous row segment a DMA lane group fetches is one full
 // 128-byte line.
 constexpr int BK2 = 64;
@@ -237,59 +241,78 @@ __device__ __forceinline__ void zero_acc(f32x16_t (&acc)[4][TN]) {
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 }
 
-// Main loop over nst K-steps of 32 (two 16-k slices each).  issue(s, buf, part) enqueues this
-// wave's DMA loads of step s (one per operand for part p, p < PARTS) into a ring of NSTAGE
-// buffers.  Fragments are double-buffered in registers: the reads of the next slice are issued
-// before the MFMAs of the current one; the step barrier sits between a step's two slices so the
-// MFMAs already issued keep the matrix cores busy across it; and the DMA loads of step s+3 are
-// spread between the MFMAs of the second slice, so no burst of memory instructions stalls the
-// wave's in-order issue while the matrix pipe drains.
-template <bool A_KC, bool B_KC, int EPI, int WN, typename Issue>
-__device__ __forceinline__ void pipeline(f32x16_t (&acc)[4][WL<WN>::TN], char* smem, int nst, int wm, int wn,
-                                         int lane, Issue&& issue) {
-    using L = WL<WN>;
-    constexpr int PER = L::PER_STEP;
-    // No wait for the previous tile's epilogue stores: every vmcnt wait below bounds the number of
-    // outstanding operations, and loads complete in order among themselves, so "at most n
-    // outstanding" still means all but the last n DMA loads have landed.
+// Weight-gradient main loop over nst K-steps of 32 (two 16-k slices each), split in two so a
+// persistent workgroup can issue the next tile's first copies before the current tile's stores.
+// issue(s, buf, part) enqueues this wave's DMA loads of step s (one per operand for part p,
+// p < PARTS) into a ring of NSTAGE buffers.  dw_prologue issues steps 0..NSTAGE-2.
+template <int WN, typename Issue>
+__device__ __forceinline__ void dw_prologue(int nst, Issue&& issue) {
 #pragma unroll
     for (int s = 0; s < NSTAGE - 1; ++s)
         if (s < nst)
 #pragma unroll
-            for (int p = 0; p < L::PARTS; ++p) issue(s, s, p);
-    if (nst >= 3) wait_vm<2 * PER>();
-    else if (nst == 2) wait_vm<PER>();
-    else wait_vm<0>();
-    block_sync();
-    Frags<L::TN> f0, f1;
-    load_frags<A_KC, B_KC, EPI, WN>(f0, smem, 0, wm, wn, lane);
-    for (int s = 0; s < nst; ++s) {
-        const char* st = smem + (s & (NSTAGE - 1)) * STAGE_BYTES;
-        load_frags<A_KC, B_KC, EPI, WN>(f1, st, 1, wm, wn, lane);
-        mma_frags<L::TN>(acc, f0);
-        // Settle the slice-1 reads only after all slice-0 MFMAs are issued (the scheduling
-        // barrier keeps the compiler from hoisting the wait above them, which would expose the
-        // reads' latency); settling them here keeps the compiler from making the next MFMAs
-        // wait on the reads issued after the step barrier.
-        __builtin_amdgcn_sched_barrier(0);
-        wait_lgkm0();
-        if (s + 1 < nst) {
-            // step s+1 must have landed: only step s+2 may still be in flight
-            if (s + 2 < nst) wait_vm<PER>();
-            else wait_vm<0>();
-            block_sync();
-            load_frags<A_KC, B_KC, EPI, WN>(f0, smem + ((s + 1) & (NSTAGE - 1)) * STAGE_BYTES, 0, wm, wn, lane);
-        }
-        // every wave is past step s-1, so its buffer takes step s+3
-        const bool more = s + NSTAGE - 1 < nst;
-        const int nb = (s + NSTAGE - 1) & (NSTAGE - 1);
+            for (int p = 0; p < WL<WN>::PARTS; ++p) issue(s, s, p);
+}
+
+// vmcnt retires this wave's vector memory operations in issue order, so "at most n outstanding"
+// means all but the last n issued have completed.  ns: at least DW_STORES vector memory
+// operations (the previous tile's epilogue stores) were issued between dw_prologue and this call;
+// the waits then let those stores drain while steps 0 and 1 run.
+template <int N>
+__device__ __forceinline__ void wait_vm_ns(bool ns) {
+    if (ns) wait_vm<N + DW_STORES>();
+    else wait_vm<N>();
+}
+
+// Fragments are double-buffered in registers: the reads of the next slice are issued before the
+// MFMAs of the current one; the step barrier sits between a step's two slices so the MFMAs already
+// issued keep the matrix cores busy across it; and the DMA loads of step s+3 are spread between the
+// MFMAs of the second slice, so no burst of memory instructions stalls the wave's in-order issue
+// while the matrix pipe drains.
+template <int WN, typename Issue>
+__device__ __forceinline__ void dw_main(f32x16_t (&acc)[4][WL<WN>::TN], char* smem, int nst, bool ns, int wm,
+                                        int wn, int lane, Issue&& issue) {
+    using L = WL<WN>;
+    constexpr int PER = L::PER_STEP;
+    if (nst > 0) {
+        // step 0 landed; after it come steps 1 and 2 (if any) and the counted stores
+        if (nst >= 3) wait_vm_ns<2 * PER>(ns);
+        else if (nst == 2) wait_vm_ns<PER>(ns);
+        else wait_vm_ns<0>(ns);
+        block_sync();
+        Frags<L::TN> f0, f1;
+        load_frags<false, false, EPI_ACC_F32, WN>(f0, smem, 0, wm, wn, lane);
+        for (int s = 0; s < nst; ++s) {
+            const char* st = smem + (s & (NSTAGE - 1)) * STAGE_BYTES;
+            load_frags<false, false, EPI_ACC_F32, WN>(f1, st, 1, wm, wn, lane);
+            mma_frags<L::TN>(acc, f0);
+            // Settle the slice-1 reads only after all slice-0 MFMAs are issued (the scheduling
+            // barrier keeps the compiler from hoisting the wait above them, which would expose the
+            // reads' latency); settling them here keeps the compiler from making the next MFMAs
+            // wait on the reads issued after the step barrier.
+            __builtin_amdgcn_sched_barrier(0);
+            wait_lgkm0();
+            if (s + 1 < nst) {
+                // step s+1 must have landed: step s+2 may still be in flight, and during steps 0
+                // and 1 the counted stores (issued after step 2) as well
+                const bool early = ns && s <= 1;
+                if (s + 2 < nst) wait_vm_ns<PER>(early);
+                else wait_vm_ns<0>(early);
+                block_sync();
+                load_frags<false, false, EPI_ACC_F32, WN>(f0, smem + ((s + 1) & (NSTAGE - 1)) * STAGE_BYTES, 0, wm,
+                                                          wn, lane);
+            }
+            // every wave is past step s-1, so its buffer takes step s+3
+            const bool more = s + NSTAGE - 1 < nst;
+            const int nb = (s + NSTAGE - 1) & (NSTAGE - 1);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            mma_row<L::TN>(acc, f1, i);
-            if (more && i % (4 / L::PARTS) == 0) issue(s + NSTAGE - 1, nb, i / (4 / L::PARTS));
+            for (int i = 0; i < 4; ++i) {
+                mma_row<L::TN>(acc, f1, i);
+                if (more && i % (4 / L::PARTS) == 0) issue(s + NSTAGE - 1, nb, i / (4 / L::PARTS));
+            }
         }
     }
-    block_sync();     // every wave is done with the ring before the epilogue reuses it
+    block_sync();     // every wave is done with the ring before the next tile's copies reuse it
 }
 
 // Fragments of one 16-k slice (kk = 0..3) of a 64-k row-kernel stage.
@@ -513,54 +536,79 @@ __device__ __forceinline__ void epi_rows_quarter(const GemmArgs& a, const f32x16
     wave_sync();
 }
 
-template <int WN, int q>
-__device__ __forceinline__ void epi_dw_quarter(const GemmArgs& a, const f32x16_t (&acc)[4][WL<WN>::TN], float* ep,
-                                               int wm, int wn, int lane, float* out, int m0, int n0) {
+// Rows 16h..16h+15 of row block q of a wave's accumulators -> LDS staging [16][EPLD] floats.
+template <int q, int h, int TN, int EPLD>
+__device__ __forceinline__ void stage_half(const f32x16_t (&acc)[4][TN], float* ep, int lane) {
+    const int lc = lane & 31, lr4 = (lane >> 5) * 4;
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 8 * h; r < 8 * h + 8; ++r)
+            ep[(((r >> 2) & 1) * 8 + lr4 + (r & 3)) * EPLD + j * 32 + lc] = acc[q][j][r];
+}
+
+// Weight-gradient epilogue for rows 16h..16h+15 of row block q: float32 stores, or += with
+// MOONEP_GRAD_ACCUM.  FULL: the tile lies inside [M, N], so every store is issued unmasked and
+// the caller can count them.
+template <int WN, int q, int h, bool FULL>
+__device__ __forceinline__ void epi_dw_part(const GemmArgs& a, const f32x16_t (&acc)[4][WL<WN>::TN], float* ep,
+                                            int wm, int wn, int lane, float* out, int m0, int n0) {
     constexpr int TN = WL<WN>::TN, EPLD = WL<WN>::EPL;
-    constexpr int LPR = 8 * TN, RPI = 64 / LPR, IT = 32 / RPI;   // float4 chunks
-    stage_quarter<q, TN, EPLD>(acc, ep, lane);
+    constexpr int LPR = 8 * TN, RPI = 64 / LPR, IT = 16 / RPI;   // float4 chunks
+    stage_half<q, h, TN, EPLD>(acc, ep, lane);
     wave_sync();
     const int c = (lane % LPR) * 4;
     const int col = n0 + wn * (256 / WN) + c;
+    const int rb = m0 + wm * 128 + q * 32 + h * 16;
     if (!a.accum) {
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
             const int rr = it * RPI + lane / LPR;
-            const int row = m0 + wm * 128 + q * 32 + rr;
-            if (row < a.M && col < a.N)
+            const int row = rb + rr;
+            if (FULL || (row < a.M && col < a.N))
                 *reinterpret_cast<float4*>(out + (size_t)row * a.N + col) =
                     *reinterpret_cast<const float4*>(ep + rr * EPLD + c);
         }
         wave_sync();
         return;
     }
+    // all loads first (clamped to in-bounds addresses), then add and store
+    float4 old[IT];
+    const int lcol = min(col, a.N - 4);
 #pragma unroll
-    for (int half = 0; half < IT / 8; ++half) {
-        // all loads first (clamped to in-bounds addresses), then add and masked stores
-        float4 old[8];
-        const int lcol = min(col, a.N - 4);
+    for (int it = 0; it < IT; ++it) {
+        const int rr = it * RPI + lane / LPR;
+        const int row = min(rb + rr, a.M - 1);
+        old[it] = *reinterpret_cast<const float4*>(out + (size_t)row * a.N + lcol);
+    }
 #pragma unroll
-        for (int it = 0; it < 8; ++it) {
-            const int rr = (half * 8 + it) * RPI + lane / LPR;
-            const int row = min(m0 + wm * 128 + q * 32 + rr, a.M - 1);
-            old[it] = *reinterpret_cast<const float4*>(out + (size_t)row * a.N + lcol);
-        }
-#pragma unroll
-        for (int it = 0; it < 8; ++it) {
-            const int rr = (half * 8 + it) * RPI + lane / LPR;
-            const int row = m0 + wm * 128 + q * 32 + rr;
-            if (row < a.M && col < a.N) {
-                const float4 v = *reinterpret_cast<const float4*>(ep + rr * EPLD + c);
-                float4 o = old[it];
-                o.x += v.x;
-                o.y += v.y;
-                o.z += v.z;
-                o.w += v.w;
-                *reinterpret_cast<float4*>(out + (size_t)row * a.N + col) = o;
-            }
+    for (int it = 0; it < IT; ++it) {
+        const int rr = it * RPI + lane / LPR;
+        const int row = rb + rr;
+        if (FULL || (row < a.M && col < a.N)) {
+            const float4 v = *reinterpret_cast<const float4*>(ep + rr * EPLD + c);
+            float4 o = old[it];
+            o.x += v.x;
+            o.y += v.y;
+            o.z += v.z;
+            o.w += v.w;
+            *reinterpret_cast<float4*>(out + (size_t)row * a.N + col) = o;
         }
     }
     wave_sync();
+}
+
+template <int WN, bool FULL>
+__device__ __forceinline__ void epi_dw(const GemmArgs& a, const f32x16_t (&acc)[4][WL<WN>::TN], float* ep, int wm,
+                                       int wn, int lane, float* out, int m0, int n0) {
+    epi_dw_part<WN, 0, 0, FULL>(a, acc, ep, wm, wn, lane, out, m0, n0);
+    epi_dw_part<WN, 0, 1, FULL>(a, acc, ep, wm, wn, lane, out, m0, n0);
+    epi_dw_part<WN, 1, 0, FULL>(a, acc, ep, wm, wn, lane, out, m0, n0);
+    epi_dw_part<WN, 1, 1, FULL>(a, acc, ep, wm, wn, lane, out, m0, n0);
+    epi_dw_part<WN, 2, 0, FULL>(a, acc, ep, wm, wn, lane, out, m0, n0);
+    epi_dw_part<WN, 2, 1, FULL>(a, acc, ep, wm, wn, lane, out, m0, n0);
+    epi_dw_part<WN, 3, 0, FULL>(a, acc, ep, wm, wn, lane, out, m0, n0);
+    epi_dw_part<WN, 3, 1, FULL>(a, acc, ep, wm, wn, lane, out, m0, n0);
 }
 
 // ---------------------------------------------------------------------------
@@ -660,11 +708,20 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_rows_kernel(GemmArgs a) {
 // slot t - E.  Tiles are handed out dynamically, targets in descending row order.
 // ---------------------------------------------------------------------------
 // WHICH (2 or 13) only separates the two weight-gradient launches' kernel names in traces.
+//
+// The persistent loop is software-pipelined by one tile: after tile i's main loop, the workgroup
+// sets up tile i+1 (its id was fetched during tile i) and issues its first three steps, then
+// stages and stores tile i's result.  The stores drain while tile i+1's first copies land and its
+// first two steps run, instead of before them.
+template <int WN>
+constexpr int dw_smem() { return DW_STG + WL<WN>::WAVES * 16 * WL<WN>::EPL * 4; }
+
 template <int WN, int WHICH>
 __global__ __launch_bounds__(128 * WN, 1) void gemm_dw_kernel(GemmArgs a) {
     using L = WL<WN>;
+    constexpr bool kCounted = 256 / L::WAVES == DW_STORES;   // stores per wave fit the vmcnt waits
     extern __shared__ __attribute__((aligned(1024))) char smem[];
-    __shared__ Segment s_seg[kMaxR + 1];
+    __shared__ Segment s_seg[2][kMaxR + 1];
     __shared__ int s_tile[2];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
@@ -672,95 +729,142 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_dw_kernel(GemmArgs a) {
     const int MT = (a.M + BM - 1) / BM, NT = a.ntiles_n;
     const int per_target = MT * NT;
     const int total = (w.E + w.R * w.B) * per_target;
-    float* ep = reinterpret_cast<float*>(smem) + wave * 32 * L::EPL;
+    float* ep = reinterpret_cast<float*>(smem + DW_STG) + wave * 16 * L::EPL;
     const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds_addr(smem) + wave * L::PARTS * 1024);
 
-    for (int iter = 0;; ++iter) {
-        if (tid == 0) s_tile[iter & 1] = atomicAdd(a.counter, 1);
+    // Tile ids pass through s_tile, alternating between its two words, so a wave still reading
+    // one word is never overtaken by thread 0 writing the next id into it.
+    int fs = 0;
+    auto publish = [&](int v) {     // thread 0's value -> every thread
+        if (tid == 0) s_tile[fs] = v;
         wait_lgkm0();
         block_sync();
-        const int t = s_tile[iter & 1];
-        if (t >= total) break;
+        const int r = s_tile[fs];
+        fs ^= 1;
+        return r;
+    };
+    auto fetch = [&]() {            // next tile id from the launch's counter
+        int v = 0;
+        if (tid == 0) v = atomicAdd(a.counter, 1);
+        return publish(v);
+    };
+    // Descriptor of tile t; its row segments go to s_seg[par].  Returns false for a tile with
+    // nothing to do (an unused slot, or no rows in accumulate mode).  Target t < E is home expert
+    // t (its home rows, then its fallback replicas in plan order); t >= E is prefetch slot t - E.
+    int nseg = 0, nst = 0, m0 = 0, n0 = 0;
+    float* out = nullptr;
+    auto setup = [&](int t, int par) {
         const int target = w.dw_order[t / per_target];
         const int local = t % per_target;
         const int nt = local / MT, mt = local % MT;
-        float* out;
-        int nseg = 0;
         if (target < w.E) {
             const Segment hs = w.home_seg[target];
             const int nfb = min(max(w.fb_n[target], 0), kMaxR - 1);
             const bool has_home = seg_ok(hs, w) && hs.rows > 0;
             nseg = (has_home ? 1 : 0) + nfb;
-            if (tid == 0 && has_home) s_seg[0] = hs;
+            if (tid == 0 && has_home) s_seg[par][0] = hs;
             if (tid >= 1 && tid <= nfb) {
                 const Segment f = w.fb_seg[(size_t)target * kMaxR + tid - 1];
-                s_seg[(has_home ? 1 : 0) + tid - 1] = seg_ok(f, w) ? f : Segment{0, 0};
+                s_seg[par][(has_home ? 1 : 0) + tid - 1] = seg_ok(f, w) ? f : Segment{0, 0};
             }
             out = a.dw_home + (size_t)target * a.M * a.N;
         } else {
             const int sl = target - w.E;
-            if (w.slot_e[sl] < 0) continue;
+            if (w.slot_e[sl] < 0) return false;
             const Segment f{w.slot_row0[sl], w.slot_rows[sl]};
-            if (!seg_ok(f, w)) continue;
-            if (tid == 0) s_seg[0] = f;
+            if (!seg_ok(f, w)) return false;
+            if (tid == 0) s_seg[par][0] = f;
             nseg = 1;
             out = a.dw_slot + (size_t)sl * a.M * a.N;
         }
         wait_lgkm0();
         block_sync();
-        int nst = 0;
-        for (int i = 0; i < nseg; ++i) nst += (s_seg[i].rows + BK - 1) / BK;
-        const int m0 = mt * BM, n0 = nt * BN;
+        nst = 0;
+        for (int i = 0; i < nseg; ++i) nst += (s_seg[par][i].rows + BK - 1) / BK;
+        m0 = mt * BM;
+        n0 = nt * BN;
+        // (an expert without rows gets a zero gradient when the outputs are written)
+        return nst > 0 || !a.accum;
+    };
+
+    // DMA issue state of the tile whose steps are being issued: per-lane byte offsets of each
+    // load (k-row kk of the step, a 16-byte column chunk) from the step's first row, and a cursor
+    // over the segments; columns outside the tile clamp to the last valid chunk (their products
+    // only reach outputs the epilogue does not store), rows past a segment's end load zeros
+    uint32_t ao[L::PARTS], bo[L::PARTS];
+    int ipar = 0, iseg = 0, ikoff = 0;
+    Segment icur{0, 0};
+    auto start_issue = [&](int par) {
+#pragma unroll
+        for (int i = 0; i < L::PARTS; ++i) {
+            const int p = (wave * L::PARTS + i) * 64 + lane;
+            const int k = p >> 5, c = (p & 31) ^ ((k & 3) << 2);
+            ao[i] = 2u * (uint32_t)(k * a.lda + min(m0 + c * 8, a.M - 8));
+            bo[i] = 2u * (uint32_t)(k * a.ldb + min(n0 + c * 8, a.N - 8));
+        }
+        ipar = par;
+        iseg = 0;
+        ikoff = 0;
+        icur = s_seg[par][0];
+    };
+    auto issue = [&](int, int buf, int i) {
+        const uint32_t l = lds_wave + buf * STAGE_BYTES + i * 1024;
+        const int row = __builtin_amdgcn_readfirstlane(icur.row0 + ikoff);
+        const int left = __builtin_amdgcn_readfirstlane(icur.rows - ikoff);
+        const uint16_t* ga = a.A + (size_t)row * a.lda;
+        const uint16_t* gb = a.B + (size_t)row * a.ldb;
+        if (left >= BK) {
+            dma16s(ga, ao[i], l);
+            dma16s(gb, bo[i], l + OP_BYTES);
+        } else {    // k-row of this lane's load: ((wave * PARTS + i) * 64 + lane) / 32
+            const bool v = (wave * L::PARTS + i) * 2 + (lane >> 5) < left;
+            dma16(v ? ga + ao[i] / 2 : w.zeros, l);
+            dma16(v ? gb + bo[i] / 2 : w.zeros, l + OP_BYTES);
+        }
+        if (i == L::PARTS - 1) {    // step issued: advance the cursor
+            ikoff += BK;
+            if (ikoff >= icur.rows) {
+                ikoff = 0;
+                ++iseg;
+                if (iseg < nseg) icur = s_seg[ipar][iseg];
+            }
+        }
+    };
+
+    // first tile
+    int par = 0;
+    int t = fetch();
+    bool have = false;
+    while (t < total && !(have = setup(t, 0))) t = fetch();
+    if (have) {
+        start_issue(0);
+        dw_prologue<WN>(nst, issue);
+    }
+    bool ns = false;   // DW_STORES stores were issued after this tile's first copies
+    while (have) {
+        int nxt = 0;
+        if (tid == 0) nxt = atomicAdd(a.counter, 1);   // consumed after the main loop
         f32x16_t acc[4][L::TN];
         zero_acc<L::TN>(acc);
-        if (nst > 0) {
-            // per-lane source of each DMA load: k-row kk of the step and a 16-byte column chunk,
-            // as byte offsets from the step's first row; columns outside the tile clamp to the last
-            // valid chunk (their products only reach outputs the epilogue does not store)
-            uint32_t ao[L::PARTS], bo[L::PARTS];
-#pragma unroll
-            for (int i = 0; i < L::PARTS; ++i) {
-                const int p = (wave * L::PARTS + i) * 64 + lane;
-                const int k = p >> 5, c = (p & 31) ^ ((k & 3) << 2);
-                ao[i] = 2u * (uint32_t)(k * a.lda + min(m0 + c * 8, a.M - 8));
-                bo[i] = 2u * (uint32_t)(k * a.ldb + min(n0 + c * 8, a.N - 8));
-            }
-            // issue cursor over the segments (runs NSTAGE-1 steps ahead of the compute); rows past
-            // a segment's end, in its last step, load zeros
-            int iseg = 0, ikoff = 0;
-            Segment icur = s_seg[0];
-            pipeline<false, false, EPI_ACC_F32, WN>(acc, smem, nst, wm, wn, lane, [&](int, int buf, int i) {
-                const uint32_t l = lds_wave + buf * STAGE_BYTES + i * 1024;
-                const int row = __builtin_amdgcn_readfirstlane(icur.row0 + ikoff);
-                const int left = __builtin_amdgcn_readfirstlane(icur.rows - ikoff);
-                const uint16_t* ga = a.A + (size_t)row * a.lda;
-                const uint16_t* gb = a.B + (size_t)row * a.ldb;
-                if (left >= BK) {
-                    dma16s(ga, ao[i], l);
-                    dma16s(gb, bo[i], l + OP_BYTES);
-                } else {    // k-row of this lane's load: ((wave * PARTS + i) * 64 + lane) / 32
-                    const bool v = (wave * L::PARTS + i) * 2 + (lane >> 5) < left;
-                    dma16(v ? ga + ao[i] / 2 : w.zeros, l);
-                    dma16(v ? gb + bo[i] / 2 : w.zeros, l + OP_BYTES);
-                }
-                if (i == L::PARTS - 1) {    // step issued: advance the cursor
-                    ikoff += BK;
-                    if (ikoff >= icur.rows) {
-                        ikoff = 0;
-                        ++iseg;
-                        if (iseg < nseg) icur = s_seg[iseg];
-                    }
-                }
-            });
-        } else if (a.accum) {
-            continue;           // nothing to add
+        dw_main<WN>(acc, smem, nst, ns, wm, wn, lane, issue);
+        // this tile's output, kept while the next tile is set up
+        float* const cout = out;
+        const int cm0 = m0, cn0 = n0;
+        // next tile: descriptor, then its first three steps
+        int tn = publish(nxt);
+        bool next = false;
+        while (tn < total && !(next = setup(tn, par ^ 1))) tn = fetch();
+        if (next) {
+            start_issue(par ^ 1);
+            dw_prologue<WN>(nst, issue);
         }
-        // (an expert without rows gets a zero gradient when the outputs are written)
-        epi_dw_quarter<WN, 0>(a, acc, ep, wm, wn, lane, out, m0, n0);
-        epi_dw_quarter<WN, 1>(a, acc, ep, wm, wn, lane, out, m0, n0);
-        epi_dw_quarter<WN, 2>(a, acc, ep, wm, wn, lane, out, m0, n0);
-        epi_dw_quarter<WN, 3>(a, acc, ep, wm, wn, lane, out, m0, n0);
-        block_sync();
+        // this tile's stores; an interior tile issues exactly DW_STORES per wave
+        const bool full = kCounted && cm0 + BM <= a.M && cn0 + BN <= a.N;
+        if (full) epi_dw<WN, true>(a, acc, ep, wm, wn, lane, cout, cm0, cn0);
+        else epi_dw<WN, false>(a, acc, ep, wm, wn, lane, cout, cm0, cn0);
+        ns = full;
+        have = next;
+        par ^= 1;
     }
 }
 
@@ -817,12 +921,13 @@ static int launch_rows(int epi, int mode, const GemmArgs& a, hipStream_t s) {
 template <int WHICH>
 static int launch_dw(const GemmArgs& a, hipStream_t s) {
     constexpr int WN = MOONEP_WN_DW;
-    static bool ok = set_smem(gemm_dw_kernel<WN, WHICH>, GEMM_SMEM);
+    constexpr int smem = dw_smem<WN>();
+    static bool ok = set_smem(gemm_dw_kernel<WN, WHICH>, smem);
     if (!ok) return MOONEP_EHIP;
     hipLaunchKernelGGL(reset_counters_kernel, dim3(1), dim3(64), 0, s, a.counter, 1);
     MOONEP_LAUNCH_CHECK();
     const int grid = (num_cus() / 8) * 8;
-    hipLaunchKernelGGL((gemm_dw_kernel<WN, WHICH>), dim3(grid), dim3(128 * WN), GEMM_SMEM, s, a);
+    hipLaunchKernelGGL((gemm_dw_kernel<WN, WHICH>), dim3(grid), dim3(128 * WN), smem, s, a);
     MOONEP_LAUNCH_CHECK();
     return MOONEP_OK;
 }
