@@ -112,8 +112,6 @@ __device__ __forceinline__ void wait_lgkm0() {
     __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));
 }
 
-// k-contiguous tile [256 rows][32 k]: 16-byte chunk (r, c), c = k/8 in 0..3
-__device__ __forceinline__ int kc_pos(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
 // m/n-contiguous tile [32 k][256 mn]: 16-byte chunk (k, c), c = mn/8 in 0..31
 __device__ __forceinline__ int mn_pos(int k, int c) { return k * 32 + (c ^ ((k & 3) << 2)); }
 // k-contiguous tile [256 rows][64 k]: 16-byte chunk (r, c), c = k/8 in 0..7; sixteen consecutive
@@ -142,11 +140,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)reinterpret_cast<uintptr_t>((lds_void_t*)(p));
 }
 
-// MFMA fragment (32 rows/cols x 16 k) from a k-contiguous tile: one 16-byte read per lane
-__device__ __forceinline__ bf16x8_t frag_kc(const char* T, int rb, int kk, int lane) {
-    const int r = rb + (lane & 31), c = kk * 2 + (lane >> 5);
-    return *reinterpret_cast<const bf16x8_t*>(T + kc_pos(r, c) * 16);
-}
+// MFMA fragment (32 rows/cols x 16 k) from a k-contiguous 64-k tile: one 16-byte read per lane
 __device__ __forceinline__ bf16x8_t frag_kc8(const char* T, int rb, int kk, int lane) {
     const int r = rb + (lane & 31), c = kk * 2 + (lane >> 5);
     return *reinterpret_cast<const bf16x8_t*>(T + kc8_pos(r, c) * 16);
@@ -194,16 +188,15 @@ struct Frags {
     bf16x8_t a[4], b[TN];
 };
 
-template <bool A_KC, bool B_KC, int EPI, int WN>
+// Fragments of one 16-k slice of a weight-gradient step (both operands m/n-contiguous).
+template <int WN>
 __device__ __forceinline__ void load_frags(Frags<WL<WN>::TN>& f, const char* st, int kk, int wm, int wn, int lane) {
     const char* As = st;
     const char* Bs = st + OP_BYTES;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-        f.a[t] = A_KC ? frag_kc(As, wm * 128 + t * 32, kk, lane) : frag_mn(As, wm * 128 + t * 32, kk, lane);
+    for (int t = 0; t < 4; ++t) f.a[t] = frag_mn(As, wm * 128 + t * 32, kk, lane);
 #pragma unroll
-    for (int t = 0; t < WL<WN>::TN; ++t)
-        f.b[t] = B_KC ? frag_kc(Bs, bcol<EPI, WN>(wn, t), kk, lane) : frag_mn(Bs, bcol<EPI, WN>(wn, t), kk, lane);
+    for (int t = 0; t < WL<WN>::TN; ++t) f.b[t] = frag_mn(Bs, bcol<EPI_ACC_F32, WN>(wn, t), kk, lane);
 }
 
 template <int TN>
@@ -281,10 +274,10 @@ __device__ __forceinline__ void dw_main(f32x16_t (&acc)[4][WL<WN>::TN], char* sm
         else wait_vm_ns<0>(ns);
         block_sync();
         Frags<L::TN> f0, f1;
-        load_frags<false, false, EPI_ACC_F32, WN>(f0, smem, 0, wm, wn, lane);
+        load_frags<WN>(f0, smem, 0, wm, wn, lane);
         for (int s = 0; s < nst; ++s) {
             const char* st = smem + (s & (NSTAGE - 1)) * STAGE_BYTES;
-            load_frags<false, false, EPI_ACC_F32, WN>(f1, st, 1, wm, wn, lane);
+            load_frags<WN>(f1, st, 1, wm, wn, lane);
             mma_frags<L::TN>(acc, f0);
             // Settle the slice-1 reads only after all slice-0 MFMAs are issued (the scheduling
             // barrier keeps the compiler from hoisting the wait above them, which would expose the
@@ -299,7 +292,7 @@ __device__ __forceinline__ void dw_main(f32x16_t (&acc)[4][WL<WN>::TN], char* sm
                 if (s + 2 < nst) wait_vm_ns<PER>(early);
                 else wait_vm_ns<0>(early);
                 block_sync();
-                load_frags<false, false, EPI_ACC_F32, WN>(f0, smem + ((s + 1) & (NSTAGE - 1)) * STAGE_BYTES, 0, wm,
+                load_frags<WN>(f0, smem + ((s + 1) & (NSTAGE - 1)) * STAGE_BYTES, 0, wm,
                                                           wn, lane);
             }
             // every wave is past step s-1, so its buffer takes step s+3
@@ -715,6 +708,8 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_rows_kernel(GemmArgs a) {
 // first two steps run, instead of before them.
 template <int WN>
 constexpr int dw_smem() { return DW_STG + WL<WN>::WAVES * 16 * WL<WN>::EPL * 4; }
+static_assert(dw_smem<2>() <= ROWS_SMEM - 4096 && dw_smem<4>() <= ROWS_SMEM - 4096,
+              "weight-gradient staging plus the kernel's static LDS must fit in 160 KiB");
 
 template <int WN, int WHICH>
 __global__ __launch_bounds__(128 * WN, 1) void gemm_dw_kernel(GemmArgs a) {
