@@ -138,6 +138,28 @@ def _backward_check(cfg):
     assert rel_fro(g13, rdW13) <= TOL and rel_fro(g2, rdW2) <= TOL
 
 
+def test_side_stream_matches_default_stream():
+    """Every call runs on the stream it is handed (torch's current stream, here a second stream of
+    default priority): the whole forward and backward there give the default stream's bits."""
+    topk, gates, xb, wb13, wb2, d, plan, dest, layer = _setup(MID, training=True)
+    x, tk, g = bf16_from_bits(xb), i32(topk), f32(gates)
+    dout = bf16_from_bits(W.grad_rows(MID.R, MID.S, MID.H, 5, "bf16"))
+    ref = [layer.forward(x, tk, g).clone(), layer.backward(dout, g).clone(), layer.dw13.clone(),
+           layer.dw2.clone()]
+    torch.cuda.synchronize()
+    for t in (layer.y, layer.drecv, layer.dw13, layer.dw2):
+        t.fill_(7)                       # stale values cannot pass for results
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        got = [layer.forward(x, tk, g).clone(), layer.backward(dout, g).clone(), layer.dw13.clone(),
+               layer.dw2.clone()]
+    torch.cuda.synchronize()
+    for a, b in zip(ref, got):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+
+
 def test_backward_writes_or_accumulates():
     """Without MOONEP_GRAD_ACCUM a second backward on the same batch rewrites the same
     gradients; with it the home gradients double.  Reduce buffers are clean after each step."""
