@@ -46,6 +46,40 @@ def test_plan_tiny_sweep(lam, B):
         assert_plan_parity(dims_of(cfg, B=B, training=True), topk, training=True)
 
 
+def _degenerate_routing(kind, R, E, S, K):
+    G = E // R
+    s_idx = np.arange(S)[None, :, None]
+    r_idx = np.arange(R)[:, None, None]
+    k_idx = np.arange(K)[None, None, :]
+    if kind == "single_hot":        # every token picks experts 0..K-1 (all on rank 0)
+        t = np.broadcast_to(k_idx, (R, S, K))
+    elif kind == "own_home":        # every token stays in its own rank's home group: no replica
+        t = r_idx * G + (s_idx * K + k_idx) % G
+    elif kind == "round_robin":     # every expert gets exactly S*K*R/E pairs
+        t = (r_idx * S * K + s_idx * K + k_idx) % E
+    elif kind == "next_rank":       # every token picks the next rank's home group
+        t = ((r_idx + 1) % R) * G + (s_idx * K + k_idx) % G
+    else:
+        raise ValueError(kind)
+    return np.ascontiguousarray(t, dtype=np.int32)
+
+
+@pytest.mark.parametrize("kind", ["single_hot", "own_home", "round_robin", "next_rank"])
+@pytest.mark.parametrize("B,training", [(0, False), (2, False), (4, True)])
+def test_plan_degenerate_routings(kind, B, training):
+    """Routings at the ends of the method's range, bit-exact against the oracle: all load on one
+    rank (most replicas, fallback when slots run out), none to move, and every pair remote."""
+    R, E, S, K = 8, 64, 96, 4
+    topk = _degenerate_routing(kind, R, E, S, K)
+    say("plan degenerate", kind, B, training)
+    d = M.Dims.make(R, E, B, S, K, 8, training=training)
+    plan, dest, (ws, cu, dd, st) = assert_plan_parity(d, topk, training=training)
+    if kind in ("own_home", "round_robin", "next_rank"):
+        assert len(plan.entries) == 0          # every rank already serves exactly S*K rows
+    if kind == "single_hot":
+        assert len(plan.entries) >= R - 1      # rank 0 sheds (R-1)*S*K rows to the others
+
+
 @pytest.mark.parametrize("R,E,S,K,B,lam", [
     (8, 64, 128, 4, 2, 0.5), (8, 64, 130, 4, 8, 1.5), (2, 16, 64, 8, 1, 1.0),
     (1, 8, 32, 2, 0, 1.0), (8, 256, 64, 8, 4, 0.3), (4, 8, 65, 8, 2, 0.0), (16, 512, 96, 8, 3, 0.8),
