@@ -13,23 +13,29 @@
 // Kernel design (MI355X / CDNA4):
 //   * 256x256 output tile per workgroup, 8 waves in 2x4 (two per SIMD), each wave
 //     128x64 = 4x2 tiles of v_mfma_f32_32x32x16_bf16 (bf16 inputs, fp32 accumulation);
-//     a 4-wave 2x2 layout of 128x128 per wave is a compile-time alternative.  K step 32.
+//     a 4-wave 2x2 layout of 128x128 per wave is a compile-time alternative.
 //   * Operand tiles go HBM -> LDS with global_load_lds_dwordx4 (16 bytes per lane, no
-//     register staging), through a 4-stage ring: loads run three K steps ahead of the
-//     matrix cores; one explicit vmcnt wait and one barrier per step.
+//     register staging), addressed as a wave-uniform base in scalar registers plus a 32-bit
+//     per-lane offset.  Row kernels: 64-k stages in five 32 KiB buffers, one operand
+//     triple-buffered (loaded two stages ahead), the other double-buffered.  Weight-gradient
+//     kernel: a ring of four 32-k stages loaded three steps ahead.  One explicit vmcnt wait
+//     and one barrier per stage.
 //   * LDS tiles are XOR-swizzled in 16-byte chunks so fragment reads are bank-conflict
 //     free.  k-contiguous operands (activations, backward weights) are read with
 //     ds_read_b128; m/n-contiguous operands (forward weights, both dW operands) stay
 //     m/n-contiguous in LDS and are read with ds_read_b64_tr_b16, which hands each lane
 //     4 consecutive k of one column -- two of them make one MFMA fragment.
-//   * Persistent grid (one workgroup per CU).  Tiles are ordered group-major, then
-//     n-tile, then m-tile, and each XCD (blockIdx % 8) takes a contiguous range of them,
-//     so tiles sharing a weight or activation panel run on the same XCD together.
-//   * Masked rows/columns of a tile load from a zero row kept in the plan workspace.
+//   * Persistent grid (one workgroup per CU).  Row kernels: tiles are ordered group-major,
+//     then n-tile, then m-tile, and each XCD (blockIdx % 8) takes a contiguous range of them,
+//     so tiles sharing a weight or activation panel run on the same XCD together; rows and
+//     columns outside a tile clamp to the last valid one.  Weight-gradient kernel: tiles are
+//     handed out dynamically, largest target first, and the loop is software-pipelined by one
+//     tile (the next tile's first copies go out before this tile's stores); rows past a
+//     segment's end load from a zero block kept in the plan workspace.
 //   * Epilogues are fused and staged through LDS for 16-byte stores: SwiGLU (act =
 //     silu(gate) * up, Gt|U saved) after the gate/up GEMM; SwiGLU' (dGt, dU written over
-//     the saved Gt|U) after dA = dY W2^T; fp32 accumulate into the home or reduce-buffer
-//     gradient for dW.
+//     the saved Gt|U) after dA = dY W2^T; fp32 store or accumulate into the home or
+//     reduce-buffer gradient for dW.
 #include "common.h"
 
 namespace moonep {

@@ -20,7 +20,8 @@
 //               best-fit picks done as wave-wide argmin/argmax (at most one remote home
 //               group per rank [TC, Installation and integration]), prefetch slots or
 //               home-row fallback [TD, memory contract], cu_seqlens per rank and weight
-//               row, instance offsets, GEMM group tables and statistics.
+//               row, instance offsets, GEMM group tables, the weight-gradient work order
+//               (targets by rows, descending) and statistics.
 //   plan_dest   one wave per chunk: pair index g = chunk prefix + popcount of the lower
 //               bits of the expert's bitmap; the instance holding g gives the final row
 //               (the send side computes the receiver's position [TC, "What the technique
