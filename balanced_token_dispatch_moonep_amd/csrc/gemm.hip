@@ -27,8 +27,9 @@
 //     4 consecutive k of one column -- two of them make one MFMA fragment.
 //   * Persistent grid (one workgroup per CU).  Row kernels: tiles are ordered group-major,
 //     then n-tile, then m-tile, and each XCD (blockIdx % 8) takes a contiguous range of them,
-//     so tiles sharing a weight or activation panel run on the same XCD together; rows and
-//     columns outside a tile clamp to the last valid one.  Weight-gradient kernel: tiles are
+//     handed out in order from a per-XCD counter, so tiles sharing a weight or activation
+//     panel run on the same XCD together; rows and columns outside a tile clamp to the last
+//     valid one.  Weight-gradient kernel: tiles are
 //     handed out dynamically, largest target first, and the loop is software-pipelined by one
 //     tile (the next tile's first copies go out before this tile's stores); rows past a
 //     segment's end load from a zero block kept in the plan workspace.
@@ -65,6 +66,8 @@ constexpr int OP2_BYTES = 256 * BK2 * 2;          // 32 KiB
 constexpr int ROWS_SMEM = 5 * OP2_BYTES;          // 160 KiB
 constexpr int MAX_GROUPS = 2 * kMaxE;
 static_assert(4 * 32 * 132 * 4 <= GEMM_SMEM, "epilogue staging must fit in the stage ring");
+static_assert(8 * 32 * 68 * 4 <= 4 * 32768 && 4 * 32 * 132 * 4 <= 4 * 32768,
+              "row-kernel epilogue staging must end below the fifth operand buffer");
 
 enum Epi { EPI_SWIGLU_FWD = 0, EPI_STORE = 1, EPI_SWIGLU_BWD = 2, EPI_ACC_F32 = 3 };
 enum Mode { ROWS_BN = 0, ROWS_BK = 1 };   // weights n-contiguous ([K, N]) or k-contiguous ([N, K])
@@ -86,7 +89,7 @@ struct GemmArgs {
     float* dw_home;           // EPI_ACC_F32: [E, M, N]
     float* dw_slot;           // EPI_ACC_F32: [R*B, M, N]
     int ntiles_n;
-    int* counter;             // dW: tile counter (zero at launch)
+    int* counter;             // tile counter(s), zero at launch (dW: one; row kernels: one per XCD)
     int accum;                // dW: add into the outputs (1) or write them (0)
 };
 
@@ -625,13 +628,34 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_rows_kernel(GemmArgs a) {
     const int NT = a.ntiles_n;
     const int total = tp[ng] * NT;
     const int nxcd = 8;
-    const int xcd = blockIdx.x % nxcd, li = blockIdx.x / nxcd, per_wg = gridDim.x / nxcd;
+    const int xcd = blockIdx.x % nxcd;
     const int chunk = (total + nxcd - 1) / nxcd;
     const int t_lo = xcd * chunk, t_hi = min(total, t_lo + chunk);
     float* ep = reinterpret_cast<float*>(smem) + wave * 32 * L::EPL;
     const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds_addr(smem) + wave * 2 * L::PARTS * 1024);
 
-    for (int t = t_lo + li; t < t_hi; t += per_wg) {
+    // The tiles of this XCD's range are handed out in order from a per-XCD counter, so the tiles
+    // in flight on an XCD stay neighbours (sharing A rows and weight columns in its L2) even when
+    // tiles take different times.  Tile ids pass through two words at the start of the fifth
+    // operand buffer, alternating: between a tile's last barrier and the next tile's first one no
+    // copy targets that buffer (the first copies go to the first stage's buffers and the deep
+    // operand's second stage), and the epilogue staging ends below it.  All 160 KiB of LDS are
+    // dynamic, so no static LDS is left for them.
+    int* const s_t = reinterpret_cast<int*>(smem + 4 * OP2_BYTES);
+    int fs = 0;
+    auto publish = [&](int v) {
+        if (tid == 0) s_t[fs] = v;
+        wait_lgkm0();
+        block_sync();
+        const int r = s_t[fs];
+        fs ^= 1;
+        return r;
+    };
+    int* const qc = a.counter + xcd;
+    int nxt = 0;
+    if (tid == 0) nxt = atomicAdd(qc, 1);
+    for (int t = t_lo + publish(nxt); t < t_hi; t = t_lo + publish(nxt)) {
+        if (tid == 0) nxt = atomicAdd(qc, 1);   // the next tile, consumed after this one
         int lo = 0, hi = ng - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
@@ -899,9 +923,14 @@ static bool set_smem(K kernel, int bytes) {
 #define MOONEP_WN_DW 4
 #endif
 
-static int launch_rows(int epi, int mode, const GemmArgs& a, hipStream_t s) {
+// Resets the eight per-XCD tile counters, then runs a row kernel.
+static int launch_rows(int epi, int mode, const GemmArgs& a0, hipStream_t s) {
     const int grid = (num_cus() / 8) * 8;
     constexpr int WN = MOONEP_WN_ROWS;
+    GemmArgs a = a0;
+    a.counter = a.w.counters + 8;
+    hipLaunchKernelGGL(reset_counters_kernel, dim3(1), dim3(64), 0, s, a.counter, 8);
+    MOONEP_LAUNCH_CHECK();
 #define MOONEP_ROWS(M_, E_)                                                                            \
     do {                                                                                               \
         static bool ok = set_smem(gemm_rows_kernel<M_, E_, WN>, ROWS_SMEM);                            \
