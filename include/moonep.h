@@ -110,8 +110,9 @@ size_t moonep_plan_workspace_bytes(const moonep_dims_t* dims);
  *   topk       [R, S, K] int32  expert ids chosen by the router for each token (k order kept)
  *   plan_ws    workspace of moonep_plan_workspace_bytes() bytes; stays valid (and is read by
  *              prefetch / grouped_ffn / reduce_grad) until the next moonep_plan on it.
- *              grouped_ffn_backward also uses two words of it as tile counters, so two
- *              backward calls on one workspace must not run concurrently.
+ *              grouped_ffn and grouped_ffn_backward also use words of it as tile counters
+ *              (reset on the stream before each GEMM phase), so FFN calls on one workspace
+ *              must not run concurrently.
  *   cu_seqlens [R, E+B+1] int32 out: per rank, prefix sums of the rows served by each weight
  *              row (home rows [0,E), slot rows [E,E+B)); cu_seqlens[q][E+B] == S*K
  *   dest       [R, S, K] int32 out: absolute row in the [R*S*K] receive buffer where the
@@ -196,8 +197,8 @@ int moonep_grouped_ffn(const moonep_dims_t* dims, const void* plan_ws, const int
  *   hold (e.g. accumulation over micro-batches; the reduce slots are zero after
  *   moonep_reduce_grad).
  * Phases (flags): MOONEP_PHASE_DACT, MOONEP_PHASE_DX, MOONEP_PHASE_DW2, MOONEP_PHASE_DW13.
- * gu_save holds Gt|U until MOONEP_PHASE_DACT has run and dGt|dU afterwards.  The two
- * weight-gradient phases use tile counters in plan_ws: calls on one plan_ws must not overlap. */
+ * gu_save holds Gt|U until MOONEP_PHASE_DACT has run and dGt|dU afterwards.  The
+ * GEMM phases use tile counters in plan_ws: FFN calls on one plan_ws must not overlap. */
 int moonep_grouped_ffn_backward(const moonep_dims_t* dims, const void* plan_ws,
                                 const int32_t* cu_seqlens, const void* recv,
                                 const void* gu_save, const void* act, const void* dy,
