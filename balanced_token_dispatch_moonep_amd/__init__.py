@@ -3,6 +3,7 @@
 Thin ctypes marshalling only: every function here checks tensor shapes, dtypes,
 devices and contiguity, then passes raw device pointers and the current HIP
 stream to the C entry point of the same name (declared in include/moonep.h).
+Tensors must live on the current device, and an explicit stream must belong to it.
 All computation happens in the library's HIP kernels; there is no Python or
 CPU fallback, and importing this package fails loudly if the library was not
 built (``python -m balanced_token_dispatch_moonep_amd.build``).
@@ -91,7 +92,8 @@ def _load():
     L.moonep_grouped_ffn_backward.argtypes = [P] + [VP] * 16
     L.moonep_reduce_grad.argtypes = [P, VP, VP, VP, VP, VP, VP]
     for n in ("moonep_plan", "moonep_prefetch", "moonep_dispatch", "moonep_combine",
-              "moonep_grouped_ffn", "moonep_grouped_ffn_backward", "moonep_reduce_grad"):
+              "moonep_dispatch_staged", "moonep_combine_staged", "moonep_grouped_ffn",
+              "moonep_grouped_ffn_backward", "moonep_reduce_grad"):
         getattr(L, n).restype = I32
     L.moonep_strerror.argtypes = [I32]
     L.moonep_strerror.restype = ctypes.c_char_p
@@ -151,6 +153,9 @@ def _ptr(t, name, dtype=None, shape=None, numel=None, optional=False):
         raise TypeError(f"{name} must be a torch.Tensor")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor (the library has no CPU path)")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}; the library runs on the current device "
+                         f"cuda:{torch.cuda.current_device()}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
@@ -160,6 +165,11 @@ def _ptr(t, name, dtype=None, shape=None, numel=None, optional=False):
     if numel is not None and t.numel() != numel:
         raise ValueError(f"{name} must have {numel} elements, got {t.numel()}")
     return t.data_ptr()
+
+
+def _ws(d: Dims, plan_ws):
+    """The plan workspace: uint8, exactly moonep_plan_workspace_bytes(d) bytes."""
+    return _ptr(plan_ws, "plan_ws", _torch().uint8, numel=moonep_plan_workspace_bytes(d))
 
 
 def _check(rc: int, where: str) -> None:
@@ -187,7 +197,7 @@ def moonep_plan(d: Dims, topk, plan_ws, cu_seqlens, dest, stats, stream=None) ->
     torch = _torch()
     args = (
         _ptr(topk, "topk", torch.int32, (d.R, d.S, d.K)),
-        _ptr(plan_ws, "plan_ws", torch.uint8, numel=moonep_plan_workspace_bytes(d)),
+        _ws(d, plan_ws),
         _ptr(cu_seqlens, "cu_seqlens", torch.int32, (d.R, d.E + d.B + 1)),
         _ptr(dest, "dest", torch.int32, (d.R, d.S, d.K)),
         _ptr(stats, "stats", torch.int32, (NSTATS,)),
@@ -199,7 +209,7 @@ def moonep_prefetch(d: Dims, plan_ws, w13_home, w2_home, w13_slot, w2_slot, stre
     torch = _torch()
     bf = torch.bfloat16
     args = (
-        _ptr(plan_ws, "plan_ws", torch.uint8),
+        _ws(d, plan_ws),
         _ptr(w13_home, "w13_home", bf, (d.E, d.H, 2 * d.I)),
         _ptr(w2_home, "w2_home", bf, (d.E, d.I, d.H)),
         _ptr(w13_slot, "w13_slot", bf, (d.R, d.B, d.H, 2 * d.I), optional=d.B == 0),
@@ -268,7 +278,7 @@ def moonep_grouped_ffn(d: Dims, plan_ws, cu_seqlens, recv, w13_home, w2_home, w1
     bf = torch.bfloat16
     M = d.R * d.S * d.K
     args = (
-        _ptr(plan_ws, "plan_ws", torch.uint8),
+        _ws(d, plan_ws),
         _ptr(cu_seqlens, "cu_seqlens", torch.int32, (d.R, d.E + d.B + 1)),
         _ptr(recv, "recv", bf, (M, d.H)),
         _ptr(w13_home, "w13_home", bf, (d.E, d.H, 2 * d.I)),
@@ -291,7 +301,7 @@ def moonep_grouped_ffn_backward(d: Dims, plan_ws, cu_seqlens, recv, gu_save, act
     M = d.R * d.S * d.K
     nb = d.B == 0
     args = (
-        _ptr(plan_ws, "plan_ws", torch.uint8),
+        _ws(d, plan_ws),
         _ptr(cu_seqlens, "cu_seqlens", torch.int32, (d.R, d.E + d.B + 1)),
         _ptr(recv, "recv", bf, (M, d.H)),
         _ptr(gu_save, "gu_save", bf, (M, 2 * d.I)),
@@ -316,7 +326,7 @@ def moonep_reduce_grad(d: Dims, plan_ws, dw13_home, dw2_home, dw13_red, dw2_red,
     f32 = torch.float32
     nb = d.B == 0
     args = (
-        _ptr(plan_ws, "plan_ws", torch.uint8),
+        _ws(d, plan_ws),
         _ptr(dw13_home, "dw13_home", f32, (d.E, d.H, 2 * d.I)),
         _ptr(dw2_home, "dw2_home", f32, (d.E, d.I, d.H)),
         _ptr(dw13_red, "dw13_red", f32, (d.R, d.B, d.H, 2 * d.I), optional=nb),

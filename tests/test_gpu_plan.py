@@ -370,3 +370,20 @@ def test_plan_dispatch_combine_max_dims():
     torch.cuda.synchronize()
     assert bits_of(recv).tobytes() == O.dispatch(dest, x).tobytes()
     assert max_row_rel(f64_of(out), O.combine(dest, O.dispatch(dest, x), gates)) <= 1e-2
+
+
+def test_binding_rejects_wrong_workspace():
+    """Every entry point that reads the plan workspace checks its size before any launch."""
+    say("binding: workspace size checks")
+    d = M.Dims.make(R=2, E=4, B=1, S=64, K=2, H=64, I=64, training=True)
+    n = M.moonep_plan_workspace_bytes(d)
+    for size in (n - 256, n + 256):
+        bad = torch.zeros(size, dtype=torch.uint8, device=DEV)
+        topk = torch.zeros((d.R, d.S, d.K), dtype=torch.int32, device=DEV)
+        for call in (lambda: M.moonep_plan(d, topk, bad, None, None, None),
+                     lambda: M.moonep_prefetch(d, bad, None, None, None, None),
+                     lambda: M.moonep_grouped_ffn(d, bad, *[None] * 9),
+                     lambda: M.moonep_grouped_ffn_backward(d, bad, *[None] * 14),
+                     lambda: M.moonep_reduce_grad(d, bad, None, None, None, None)):
+            with pytest.raises(ValueError, match="plan_ws"):
+                call()
