@@ -144,6 +144,18 @@ __device__ __forceinline__ void dma16s(const uint16_t* base, uint32_t voff, uint
                  : "memory", "m0");
 }
 #pragma clang diagnostic pop
+// Next ticket of a tile counter.  An atomic increment rather than an add: the compiler rewrites
+// an atomic add into a wave-reduced form that reads the result back at once, i.e. it waits there
+// for every memory operation the wave has in flight; the increment's result is awaited only
+// where it is used.
+__device__ __forceinline__ int take_ticket(int* c) {
+    return (int)atomicInc(reinterpret_cast<unsigned*>(c), 0xFFFFFFFFu);
+}
+// Scalar (wave-uniform) load of data that no kernel of this launch writes: the address must be
+// the same for every lane; read through the constant address space, so it becomes a scalar load.
+__device__ __forceinline__ int sload(const int32_t* p) {
+    return *(const __attribute__((address_space(4))) int32_t*)(p);
+}
 // LDS byte address of a pointer into dynamic shared memory
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)reinterpret_cast<uintptr_t>((lds_void_t*)(p));
@@ -647,24 +659,29 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_rows_kernel(GemmArgs a) {
         if (tid == 0) s_t[fs] = v;
         wait_lgkm0();
         block_sync();
-        const int r = s_t[fs];
+        const int r = __builtin_amdgcn_readfirstlane(s_t[fs]);
         fs ^= 1;
         return r;
     };
     int* const qc = a.counter + xcd;
     int nxt = 0;
-    if (tid == 0) nxt = atomicAdd(qc, 1);
+    if (tid == 0) nxt = take_ticket(qc);
     for (int t = t_lo + publish(nxt); t < t_hi; t = t_lo + publish(nxt)) {
-        if (tid == 0) nxt = atomicAdd(qc, 1);   // the next tile, consumed after this one
+        if (tid == 0) nxt = take_ticket(qc);   // the next tile, read after this tile's main loop
+        // the tile's group, by binary search over the tile prefix; scalar loads (the search is
+        // wave-uniform), which do not wait for the previous tile's stores and stay in the scalar
+        // cache after the first tile
         int lo = 0, hi = ng - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
-            if (tp[mid] * NT <= t) lo = mid; else hi = mid - 1;
+            if (sload(tp + mid) * NT <= t) lo = mid; else hi = mid - 1;
         }
         const int g = lo;
-        const Group gr = groups[g];
-        const int mtiles = tp[g + 1] - tp[g];
-        const int local = t - tp[g] * NT;
+        const Group gr{sload(&groups[g].row0), sload(&groups[g].rows), sload(&groups[g].wsel),
+                       sload(&groups[g].expert)};
+        const int tpg = sload(tp + g);
+        const int mtiles = sload(tp + g + 1) - tpg;
+        const int local = t - tpg * NT;
         const int nt = local / mtiles, mt = local % mtiles;
         const int row0 = gr.row0 + mt * BM;
         const int mvalid = min(BM, group_rows(gr, a.w) - mt * BM);
@@ -716,6 +733,10 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_rows_kernel(GemmArgs a) {
                 else dma16s(W + (size_t)s * bstep, bo[i], l);
             }
         });
+        // the next tile's ticket is read here, while no stores are in flight: vmcnt retires in
+        // order, so awaiting it after the epilogue would wait for all of the epilogue's stores
+        // (every wave reads it, so none carries it as outstanding into the next tile)
+        nxt = __builtin_amdgcn_readfirstlane(nxt);
         epi_rows_quarter<EPI, WN, 0>(a, acc, ep, wm, wn, lane, nt, row0, mvalid);
         epi_rows_quarter<EPI, WN, 1>(a, acc, ep, wm, wn, lane, nt, row0, mvalid);
         epi_rows_quarter<EPI, WN, 2>(a, acc, ep, wm, wn, lane, nt, row0, mvalid);
