@@ -46,7 +46,8 @@ KERNEL_NAMES = {
     "combine_bwd": "moonep::combine_kernel<false, false, 7, false>",
     "reduce_grad": "moonep::reduce_grad_kernel",
 }
-# sources each kernel is compiled from (a change to any of them voids its stored counters)
+# sources each kernel is compiled from (a code change to any of them, comments aside, voids its
+# stored counters)
 KERNEL_SOURCES = {
     "prefetch": ("weights.hip",), "reduce_grad": ("weights.hip",),
     "dispatch": ("permute.hip",), "combine": ("permute.hip",),
@@ -474,14 +475,24 @@ def roofline_of(name, w, ms):
             "operand_bytes": w[2]}
 
 
+def _code_only(text):
+    """C++ source without comments and blank lines (string literals in these sources hold no
+    comment markers), so that a comment edit does not count as a kernel change."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(l.rstrip() for l in text.splitlines() if l.strip())
+
+
 def _sources_digest(call):
+    """Digest of the code (comments excluded) of the call's kernel sources."""
     import hashlib
     csrc = os.path.join(ROOT, "balanced_token_dispatch_moonep_amd", "csrc")
     files = KERNEL_SOURCES.get(call, ("gemm.hip",)) + ("common.h",)
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

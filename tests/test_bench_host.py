@@ -62,3 +62,11 @@ def test_group_stats():
     # groups of 300, 256 and 100 rows -> 2 + 1 + 1 tiles of 256 rows, 656 real rows of 1024
     assert g == {"groups": 3, "row_tiles": 4, "padding_frac": round(1 - 656 / 1024, 4)}
     assert bench.group_stats(np.zeros((2, 4), dtype=np.int64))["groups"] == 0
+
+
+def test_traffic_digest_ignores_comments_only():
+    """Stored counter traffic stays valid across comment edits and is voided by a code change."""
+    a = "int a = 1;  // one\nint b = 2;\n"
+    b = "// header\nint a = 1;\n/* two\n   lines */\nint b = 2;   \n"
+    assert bench._code_only(a) == bench._code_only(b)
+    assert bench._code_only(a) != bench._code_only("int a = 3;\nint b = 2;\n")
