@@ -68,6 +68,8 @@ constexpr int MAX_GROUPS = 2 * kMaxE;
 static_assert(4 * 32 * 132 * 4 <= GEMM_SMEM, "epilogue staging must fit in the stage ring");
 static_assert(8 * 32 * 68 * 4 <= 4 * 32768 && 4 * 32 * 132 * 4 <= 4 * 32768,
               "row-kernel epilogue staging must end below the fifth operand buffer");
+static_assert(8 * 32 * 68 * 4 <= 3 * 32768 && 3 * 32768 + 8 * 8192 <= 5 * 32768,
+              "dA epilogue: staging below the fourth operand buffer, Gt|U copies in the last two");
 
 enum Epi { EPI_SWIGLU_FWD = 0, EPI_STORE = 1, EPI_SWIGLU_BWD = 2, EPI_ACC_F32 = 3 };
 enum Mode { ROWS_BN = 0, ROWS_BK = 1 };   // weights n-contiguous ([K, N]) or k-contiguous ([N, K])
@@ -468,9 +470,33 @@ __device__ __forceinline__ void read8(const float* p, float (&v)[8]) {
     v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w; v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
 }
 
+// dA epilogue: DMA of quarter q's saved Gt|U into the wave's 8 KiB LDS region (an operand buffer
+// the epilogue does not use): chunk (it, gate/up) of lane l lands at region + (2 it + u) KiB +
+// 16 l, holding the (row, columns) that lane reads in the epilogue; rows and columns outside the
+// tile clamp to the last valid one.  Copied rather than loaded so that it can be issued ahead of
+// the previous quarter's stores without holding registers: vmcnt retires in order, so a load
+// issued after those stores would wait for them.
+template <int WN, int q>
+__device__ __forceinline__ void prefetch_gu(const GemmArgs& a, int wm, int wn, int lane, int nt, int row0,
+                                            int mvalid, uint32_t region) {
+    constexpr int TN = WL<WN>::TN;
+    constexpr int LPR = 4 * TN, RPI = 64 / LPR, IT = 32 / RPI;
+    const int I = a.I;
+    const int lcol = min(nt * BN + wn * (256 / WN) + (lane % LPR) * 8, I - 8);
+    const int rbase = wm * 128 + q * 32;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const size_t row = (size_t)(row0 + min(rbase + it * RPI + lane / LPR, mvalid - 1));
+        dma16(a.gu + row * 2 * I + lcol, region + (2 * it) * 1024);
+        dma16(a.gu + row * 2 * I + I + lcol, region + (2 * it + 1) * 1024);
+    }
+}
+
 template <int EPI, int WN, int q>
 __device__ __forceinline__ void epi_rows_quarter(const GemmArgs& a, const f32x16_t (&acc)[4][WL<WN>::TN], float* ep,
-                                                 int wm, int wn, int lane, int nt, int row0, int mvalid) {
+                                                 int wm, int wn, int lane, int nt, int row0, int mvalid,
+                                                 const char* gl = nullptr, uint32_t gu_lds = 0,
+                                                 bool gfull = false) {
     constexpr int TN = WL<WN>::TN, EPLD = WL<WN>::EPL;
     stage_quarter<q, TN, EPLD>(acc, ep, lane);
     wave_sync();
@@ -504,16 +530,18 @@ __device__ __forceinline__ void epi_rows_quarter(const GemmArgs& a, const f32x16
         const int I = a.I;
         const int c = (lane % LPR) * 8;
         const int col = nt * BN + wn * (256 / WN) + c;
-        // all loads first (clamped to in-bounds addresses), then compute and masked stores
+        // this quarter's Gt|U has landed in the wave's LDS region: in a full tile only the
+        // previous quarter's 2 IT stores were issued after its copy
+        if (q > 0 && gfull) wait_vm<2 * IT>();
+        else wait_vm<0>();
         uint4 gv[IT], uv[IT];
-        const int lcol = min(col, I - 8);
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
-            const int rr = it * RPI + lane / LPR;
-            const size_t row = (size_t)(row0 + min(rbase + rr, mvalid - 1));
-            gv[it] = *reinterpret_cast<const uint4*>(a.gu + row * 2 * I + lcol);
-            uv[it] = *reinterpret_cast<const uint4*>(a.gu + row * 2 * I + I + lcol);
+            gv[it] = *reinterpret_cast<const uint4*>(gl + (2 * it) * 1024 + lane * 16);
+            uv[it] = *reinterpret_cast<const uint4*>(gl + (2 * it + 1) * 1024 + lane * 16);
         }
+        wait_lgkm0();   // the region is free again: the next quarter's copy goes out before the stores
+        if constexpr (q < 3) prefetch_gu<WN, q + 1>(a, wm, wn, lane, nt, row0, mvalid, gu_lds);
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
             const int rr = it * RPI + lane / LPR;
@@ -737,10 +765,16 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_rows_kernel(GemmArgs a) {
         // order, so awaiting it after the epilogue would wait for all of the epilogue's stores
         // (every wave reads it, so none carries it as outstanding into the next tile)
         nxt = __builtin_amdgcn_readfirstlane(nxt);
-        epi_rows_quarter<EPI, WN, 0>(a, acc, ep, wm, wn, lane, nt, row0, mvalid);
-        epi_rows_quarter<EPI, WN, 1>(a, acc, ep, wm, wn, lane, nt, row0, mvalid);
-        epi_rows_quarter<EPI, WN, 2>(a, acc, ep, wm, wn, lane, nt, row0, mvalid);
-        epi_rows_quarter<EPI, WN, 3>(a, acc, ep, wm, wn, lane, nt, row0, mvalid);
+        // dA: the saved Gt|U goes through the last two operand buffers (8 KiB per wave), which
+        // the epilogue staging does not reach; quarter 0's copy goes out now
+        const char* gl = smem + 3 * OP2_BYTES + wave * 8192;
+        const uint32_t gu_lds = __builtin_amdgcn_readfirstlane(lds_addr(gl));
+        const bool gfull = mvalid >= BM && nt * BN + BN <= a.I;
+        if constexpr (EPI == EPI_SWIGLU_BWD) prefetch_gu<WN, 0>(a, wm, wn, lane, nt, row0, mvalid, gu_lds);
+        epi_rows_quarter<EPI, WN, 0>(a, acc, ep, wm, wn, lane, nt, row0, mvalid, gl, gu_lds, gfull);
+        epi_rows_quarter<EPI, WN, 1>(a, acc, ep, wm, wn, lane, nt, row0, mvalid, gl, gu_lds, gfull);
+        epi_rows_quarter<EPI, WN, 2>(a, acc, ep, wm, wn, lane, nt, row0, mvalid, gl, gu_lds, gfull);
+        epi_rows_quarter<EPI, WN, 3>(a, acc, ep, wm, wn, lane, nt, row0, mvalid, gl, gu_lds, gfull);
         block_sync();   // the ring is reused by the next tile's loads
     }
 }
