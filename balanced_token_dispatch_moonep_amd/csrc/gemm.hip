@@ -68,8 +68,8 @@ constexpr int MAX_GROUPS = 2 * kMaxE;
 static_assert(4 * 32 * 132 * 4 <= GEMM_SMEM, "epilogue staging must fit in the stage ring");
 static_assert(8 * 32 * 68 * 4 <= 4 * 32768 && 4 * 32 * 132 * 4 <= 4 * 32768,
               "row-kernel epilogue staging must end below the fifth operand buffer");
-static_assert(8 * 32 * 68 * 4 <= 3 * 32768 && 3 * 32768 + 8 * 8192 <= 5 * 32768,
-              "dA epilogue: staging below the fourth operand buffer, Gt|U copies in the last two");
+static_assert(8 * 32 * 68 * 4 <= 3 * 32768 && 4 * 32 * 132 * 4 <= 3 * 32768,
+              "dA epilogue: staging below the fourth operand buffer (Gt|U copies use the last two)");
 
 enum Epi { EPI_SWIGLU_FWD = 0, EPI_STORE = 1, EPI_SWIGLU_BWD = 2, EPI_ACC_F32 = 3 };
 enum Mode { ROWS_BN = 0, ROWS_BK = 1 };   // weights n-contiguous ([K, N]) or k-contiguous ([N, K])
@@ -470,8 +470,8 @@ __device__ __forceinline__ void read8(const float* p, float (&v)[8]) {
     v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w; v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
 }
 
-// dA epilogue: DMA of quarter q's saved Gt|U into the wave's 8 KiB LDS region (an operand buffer
-// the epilogue does not use): chunk (it, gate/up) of lane l lands at region + (2 it + u) KiB +
+// dA epilogue: DMA of quarter q's saved Gt|U into the wave's LDS region (its share of the two
+// operand buffers the epilogue does not use): chunk (it, gate/up) of lane l lands at region + (2 it + u) KiB +
 // 16 l, holding the (row, columns) that lane reads in the epilogue; rows and columns outside the
 // tile clamp to the last valid one.  Copied rather than loaded so that it can be issued ahead of
 // the previous quarter's stores without holding registers: vmcnt retires in order, so a load
@@ -765,9 +765,12 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_rows_kernel(GemmArgs a) {
         // order, so awaiting it after the epilogue would wait for all of the epilogue's stores
         // (every wave reads it, so none carries it as outstanding into the next tile)
         nxt = __builtin_amdgcn_readfirstlane(nxt);
-        // dA: the saved Gt|U goes through the last two operand buffers (8 KiB per wave), which
-        // the epilogue staging does not reach; quarter 0's copy goes out now
-        const char* gl = smem + 3 * OP2_BYTES + wave * 8192;
+        // dA: the saved Gt|U goes through the last two operand buffers (64 KiB split over the
+        // waves), which the epilogue staging does not reach; quarter 0's copy goes out now
+        constexpr int GU_WAVE = 2 * OP2_BYTES / L::WAVES;
+        static_assert(GU_WAVE == 2 * 1024 * (32 / (64 / (4 * L::TN))),
+                      "a wave's Gt|U copies of one quarter fill its share of the two buffers");
+        const char* gl = smem + 3 * OP2_BYTES + wave * GU_WAVE;
         const uint32_t gu_lds = __builtin_amdgcn_readfirstlane(lds_addr(gl));
         const bool gfull = mvalid >= BM && nt * BN + BN <= a.I;
         if constexpr (EPI == EPI_SWIGLU_BWD) prefetch_gu<WN, 0>(a, wm, wn, lane, nt, row0, mvalid, gu_lds);
