@@ -37,6 +37,8 @@
 //     silu(gate) * up, Gt|U saved) after the gate/up GEMM; SwiGLU' (dGt, dU written over
 //     the saved Gt|U) after dA = dY W2^T; fp32 store or accumulate into the home or
 //     reduce-buffer gradient for dW.
+#include <type_traits>
+
 #include "common.h"
 
 namespace moonep {
@@ -298,7 +300,11 @@ __device__ __forceinline__ void dw_main(f32x16_t (&acc)[4][WL<WN>::TN], char* sm
         block_sync();
         Frags<L::TN> f0, f1;
         load_frags<WN>(f0, smem, 0, wm, wn, lane);
-        for (int s = 0; s < nst; ++s) {
+        // One step.  FAST: steps 2 .. nst-4, where step s+3 exists and the counted stores have
+        // retired from the waits; the conditions are then compile-time, so these steps carry no
+        // branch around their waits and copies.
+        auto step = [&](int s, auto fast_c) {
+            constexpr bool fast = decltype(fast_c)::value;
             const char* st = smem + (s & (NSTAGE - 1)) * STAGE_BYTES;
             load_frags<WN>(f1, st, 1, wm, wn, lane);
             mma_frags<L::TN>(acc, f0);
@@ -308,25 +314,36 @@ __device__ __forceinline__ void dw_main(f32x16_t (&acc)[4][WL<WN>::TN], char* sm
             // wait on the reads issued after the step barrier.
             __builtin_amdgcn_sched_barrier(0);
             wait_lgkm0();
-            if (s + 1 < nst) {
+            if (fast || s + 1 < nst) {
                 // step s+1 must have landed: step s+2 may still be in flight, and during steps 0
                 // and 1 the counted stores (issued after step 2) as well
-                const bool early = ns && s <= 1;
-                if (s + 2 < nst) wait_vm_ns<PER>(early);
-                else wait_vm_ns<0>(early);
+                if constexpr (fast) {
+                    wait_vm<PER>();
+                } else {
+                    const bool early = ns && s <= 1;
+                    if (s + 2 < nst) wait_vm_ns<PER>(early);
+                    else wait_vm_ns<0>(early);
+                }
                 block_sync();
-                load_frags<WN>(f0, smem + ((s + 1) & (NSTAGE - 1)) * STAGE_BYTES, 0, wm,
-                                                          wn, lane);
+                load_frags<WN>(f0, smem + ((s + 1) & (NSTAGE - 1)) * STAGE_BYTES, 0, wm, wn, lane);
             }
             // every wave is past step s-1, so its buffer takes step s+3
-            const bool more = s + NSTAGE - 1 < nst;
+            const bool more = fast || s + NSTAGE - 1 < nst;
             const int nb = (s + NSTAGE - 1) & (NSTAGE - 1);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 mma_row<L::TN>(acc, f1, i);
-                if (more && i % (4 / L::PARTS) == 0) issue(s + NSTAGE - 1, nb, i / (4 / L::PARTS));
+                if (more && i % (4 / L::PARTS) == 0) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    issue(s + NSTAGE - 1, nb, i / (4 / L::PARTS));
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
-        }
+        };
+        int s = 0;
+        for (; s < nst && s < 2; ++s) step(s, std::false_type{});
+        for (; s + NSTAGE - 1 < nst; ++s) step(s, std::true_type{});
+        for (; s < nst; ++s) step(s, std::false_type{});
     }
     block_sync();     // every wave is done with the ring before the next tile's copies reuse it
 }
@@ -374,41 +391,49 @@ __device__ __forceinline__ void pipeline64(f32x16_t (&acc)[4][WL<WN>::TN], char*
     block_sync();
     Frags<L::TN> f0, f1;
     load_frags64<B_KC, EPI, WN>(f0, smem, smem + RA * OP2_BYTES, 0, wm, wn, lane);
-    for (int s = 0; s < nst; ++s) {
+    // One stage; MORE: stage s+1 exists, MORE3: stage s+2 exists.  Compile-time flags, so the
+    // steady-state loop below carries no branch around its copies and waits.
+    auto stage = [&](int s, auto more_c, auto more3_c) {
+        constexpr bool more = decltype(more_c)::value, more3 = decltype(more3_c)::value;
         const char* As = smem + (s % RA) * OP2_BYTES;
         const char* Bs = smem + (RA + s % RB) * OP2_BYTES;
-        const bool more = s + 1 < nst, more3 = s + 2 < nst;
         // slice 0: the double-buffered operand of stage s+1
         load_frags64<B_KC, EPI, WN>(f1, As, Bs, 1, wm, wn, lane);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             mma_row<L::TN>(acc, f0, i);
-            if (i % (4 / P2 > 0 ? 4 / P2 : 1) == 0 && more)
+            if constexpr (more)
+                if (i % (4 / P2 > 0 ? 4 / P2 : 1) == 0)
 #pragma unroll
-                for (int p = 0; p < (P2 > 4 ? P2 / 4 : 1); ++p) {
-                    const int part = P2 > 4 ? i * (P2 / 4) + p : i / (4 / P2);
-                    issue(D2, s + 1, buf_of(D2, s + 1), part);
-                }
+                    for (int p = 0; p < (P2 > 4 ? P2 / 4 : 1); ++p) {
+                        const int part = P2 > 4 ? i * (P2 / 4) + p : i / (4 / P2);
+                        __builtin_amdgcn_sched_barrier(0);
+                        issue(D2, s + 1, buf_of(D2, s + 1), part);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
         }
         // slice 1: the triple-buffered operand of stage s+2
         load_frags64<B_KC, EPI, WN>(f0, As, Bs, 2, wm, wn, lane);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             mma_row<L::TN>(acc, f1, i);
-            if (i % (4 / P2 > 0 ? 4 / P2 : 1) == 0 && more3)
+            if constexpr (more3)
+                if (i % (4 / P2 > 0 ? 4 / P2 : 1) == 0)
 #pragma unroll
-                for (int p = 0; p < (P2 > 4 ? P2 / 4 : 1); ++p) {
-                    const int part = P2 > 4 ? i * (P2 / 4) + p : i / (4 / P2);
-                    issue(D3, s + 2, buf_of(D3, s + 2), part);
-                }
+                    for (int p = 0; p < (P2 > 4 ? P2 / 4 : 1); ++p) {
+                        const int part = P2 > 4 ? i * (P2 / 4) + p : i / (4 / P2);
+                        __builtin_amdgcn_sched_barrier(0);
+                        issue(D3, s + 2, buf_of(D3, s + 2), part);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
         }
         // slice 2
         load_frags64<B_KC, EPI, WN>(f1, As, Bs, 3, wm, wn, lane);
         mma_frags<L::TN>(acc, f0);
         __builtin_amdgcn_sched_barrier(0);
         wait_lgkm0();
-        if (more) {
-            if (more3) wait_vm<P2>();     // stage s+1 has landed (stage s+2's deep operand may not)
+        if constexpr (more) {
+            if constexpr (more3) wait_vm<P2>();     // stage s+1 has landed (stage s+2's deep operand may not)
             else wait_vm<0>();
             block_sync();
             load_frags64<B_KC, EPI, WN>(f0, smem + ((s + 1) % RA) * OP2_BYTES,
@@ -416,7 +441,13 @@ __device__ __forceinline__ void pipeline64(f32x16_t (&acc)[4][WL<WN>::TN], char*
         }
         // slice 3
         mma_frags<L::TN>(acc, f1);
-    }
+    };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    int s = 0;
+    for (; s + 2 < nst; ++s) stage(s, T_{}, T_{});
+    if (s + 1 < nst) stage(s++, T_{}, F_{});
+    if (s < nst) stage(s, F_{}, F_{});
     (void)N3;
     block_sync();     // every wave is done with the buffers before the epilogue reuses them
 }
