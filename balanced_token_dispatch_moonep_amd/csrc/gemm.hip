@@ -930,7 +930,7 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_dw_kernel(GemmArgs a) {
         const int left = __builtin_amdgcn_readfirstlane(icur.rows - ikoff);
         const uint16_t* ga = a.A + (size_t)row * a.lda;
         const uint16_t* gb = a.B + (size_t)row * a.ldb;
-        if (left >= BK) {
+        if (__builtin_expect(left >= BK, 1)) {   // all but a segment's last step: fall-through path
             dma16s(ga, ao[i], l);
             dma16s(gb, bo[i], l + OP_BYTES);
         } else {    // k-row of this lane's load: ((wave * PARTS + i) * 64 + lane) / 32
@@ -940,7 +940,7 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_dw_kernel(GemmArgs a) {
         }
         if (i == L::PARTS - 1) {    // step issued: advance the cursor
             ikoff += BK;
-            if (ikoff >= icur.rows) {
+            if (__builtin_expect(ikoff >= icur.rows, 0)) {
                 ikoff = 0;
                 ++iseg;
                 if (iseg < nseg) icur = s_seg[ipar][iseg];
