@@ -287,9 +287,10 @@ __device__ __forceinline__ void wait_vm_ns(bool ns) {
 // issued keep the matrix cores busy across it; and the DMA loads of step s+3 are spread between the
 // MFMAs of the second slice, so no burst of memory instructions stalls the wave's in-order issue
 // while the matrix pipe drains.
-template <int WN, typename Issue>
+template <int WN, typename Issue, typename IssueFast, typename FastRun>
 __device__ __forceinline__ void dw_main(f32x16_t (&acc)[4][WL<WN>::TN], char* smem, int nst, bool ns, int wm,
-                                        int wn, int lane, Issue&& issue) {
+                                        int wn, int lane, Issue&& issue, IssueFast&& issue_fast,
+                                        FastRun&& fast_run) {
     using L = WL<WN>;
     constexpr int PER = L::PER_STEP;
     if (nst > 0) {
@@ -300,9 +301,10 @@ __device__ __forceinline__ void dw_main(f32x16_t (&acc)[4][WL<WN>::TN], char* sm
         block_sync();
         Frags<L::TN> f0, f1;
         load_frags<WN>(f0, smem, 0, wm, wn, lane);
-        // One step.  FAST: steps 2 .. nst-4, where step s+3 exists and the counted stores have
-        // retired from the waits; the conditions are then compile-time, so these steps carry no
-        // branch around their waits and copies.
+        // One step.  FAST: a step s in 2 .. nst-4 (step s+3 exists and the counted stores have
+        // retired from the waits) whose step s+3 is full and does not end its segment; the
+        // conditions are then compile-time, so these steps carry no branch around their waits and
+        // copies.
         auto step = [&](int s, auto fast_c) {
             constexpr bool fast = decltype(fast_c)::value;
             const char* st = smem + (s & (NSTAGE - 1)) * STAGE_BYTES;
@@ -335,14 +337,21 @@ __device__ __forceinline__ void dw_main(f32x16_t (&acc)[4][WL<WN>::TN], char* sm
                 mma_row<L::TN>(acc, f1, i);
                 if (more && i % (4 / L::PARTS) == 0) {
                     __builtin_amdgcn_sched_barrier(0);
-                    issue(s + NSTAGE - 1, nb, i / (4 / L::PARTS));
+                    if constexpr (fast) issue_fast(s + NSTAGE - 1, nb, i / (4 / L::PARTS));
+                    else issue(s + NSTAGE - 1, nb, i / (4 / L::PARTS));
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
         };
         int s = 0;
         for (; s < nst && s < 2; ++s) step(s, std::false_type{});
-        for (; s + NSTAGE - 1 < nst; ++s) step(s, std::true_type{});
+        // the run of full steps that the cursor's segment still holds (all of a one-segment
+        // target's steps but its last), then everything else the general way
+        if (s + NSTAGE - 1 < nst) {
+            const int e = s + max(0, min(nst - (NSTAGE - 1) - s, fast_run()));
+            for (; s < e; ++s) step(s, std::true_type{});
+        }
+        for (; s + NSTAGE - 1 < nst; ++s) step(s, std::false_type{});
         for (; s < nst; ++s) step(s, std::false_type{});
     }
     block_sync();     // every wave is done with the ring before the next tile's copies reuse it
@@ -947,6 +956,16 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_dw_kernel(GemmArgs a) {
             }
         }
     };
+    // A full step that does not end its segment (more than BK rows left): no branches.
+    auto issue_fast = [&](int, int buf, int i) {
+        const uint32_t l = lds_wave + buf * STAGE_BYTES + i * 1024;
+        const int row = __builtin_amdgcn_readfirstlane(icur.row0 + ikoff);
+        dma16s(a.A + (size_t)row * a.lda, ao[i], l);
+        dma16s(a.B + (size_t)row * a.ldb, bo[i], l + OP_BYTES);
+        if (i == L::PARTS - 1) ikoff += BK;
+    };
+    // how many steps issue_fast may issue in a row from the cursor
+    auto fast_run = [&]() { return __builtin_amdgcn_readfirstlane((icur.rows - ikoff - 1) / BK); };
 
     // first tile
     int par = 0;
@@ -964,7 +983,7 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_dw_kernel(GemmArgs a) {
                                                        // add on purpose: see the loop's header)
         f32x16_t acc[4][L::TN];
         zero_acc<L::TN>(acc);
-        dw_main<WN>(acc, smem, nst, ns, wm, wn, lane, issue);
+        dw_main<WN>(acc, smem, nst, ns, wm, wn, lane, issue, issue_fast, fast_run);
         // this tile's output, kept while the next tile is set up
         float* const cout = out;
         const int cm0 = m0, cn0 = n0;
