@@ -53,7 +53,8 @@ __device__ __forceinline__ uint4 scale_vec(uint4 v, float g) {
 // scale loads out of the store loop; the unscaled form reads its destinations in the loop
 // (measured faster).
 // IDENT: dest[p] = p (rows land in arrival order: the first copy of the staged baseline).
-template <bool F32, bool SCALE, int KT, int VB, bool IDENT = false>
+// FULL: the row is a whole number of batches (64 VB vectors), so no vector needs a bounds check.
+template <bool F32, bool SCALE, int KT, int VB, bool IDENT = false, bool FULL = false>
 __global__ __launch_bounds__(256) void dispatch_kernel(const int32_t* __restrict__ dest,
                                                        const uint4* __restrict__ src,
                                                        const float* __restrict__ scale,
@@ -81,7 +82,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const int32_t* __restrict
 #pragma unroll
         for (int u = 0; u < VB; ++u) {
             const int v = v0 + u * 64 + lane;
-            if (v < rowvec) x[u] = ld_nt(s + v);
+            if (FULL || v < rowvec) x[u] = ld_nt(s + v);
         }
         auto put = [&](int d, float g) {
             if ((unsigned long long)(long long)d >= (unsigned long long)nrows) return;
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const int32_t* __restrict
 #pragma unroll
             for (int u = 0; u < VB; ++u) {
                 const int v = v0 + u * 64 + lane;
-                if (v < rowvec) o[v] = scale_vec<F32, SCALE>(x[u], g);
+                if (FULL || v < rowvec) o[v] = scale_vec<F32, SCALE>(x[u], g);
             }
         };
         if constexpr (KT > 0) {
@@ -125,7 +126,8 @@ __device__ __forceinline__ void acc_vec(float* a, uint4 v, float g) {
 // are read one after another, VB KiB of one row at a time (measured faster than keeping all K
 // rows' loads in flight, which spreads each wave over K places of HBM at once).
 // IDENT: dest[p] = p (rows read in arrival order: the reduction of the staged baseline).
-template <bool F32, bool GATES, int VB, bool IDENT = false>
+// FULL: as for dispatch_kernel.
+template <bool F32, bool GATES, int VB, bool IDENT = false, bool FULL = false>
 __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ dest,
                                                       const uint4* __restrict__ y,
                                                       const float* __restrict__ gates,
@@ -153,13 +155,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
 #pragma unroll
             for (int u = 0; u < VB; ++u) {
                 const int v = v0 + u * 64 + lane;
-                if (v < rowvec) acc_vec<F32>(acc[u], ld_nt(yr + v), g);
+                if (FULL || v < rowvec) acc_vec<F32>(acc[u], ld_nt(yr + v), g);
             }
         }
 #pragma unroll
         for (int u = 0; u < VB; ++u) {
             const int v = v0 + u * 64 + lane;
-            if (v >= rowvec) continue;
+            if (!FULL && v >= rowvec) continue;
             uint4 r;
             if constexpr (F32) {
                 r = make_uint4(__float_as_uint(acc[u][0]), __float_as_uint(acc[u][1]), __float_as_uint(acc[u][2]),
@@ -177,19 +179,26 @@ template <bool F32, bool SCALE, bool IDENT = false>
 static void launch_dispatch(int K, dim3 grid, hipStream_t s, const int32_t* dest, const uint4* src,
                             const float* scale, uint4* recv, int ntok, int rowvec, long long nrows) {
     constexpr int VB = SCALE ? MOONEP_DISPATCH_SCALED_VB : MOONEP_DISPATCH_VB;
+    const bool full = rowvec % (64 * VB) == 0;   // (measured neutral here; fewer instructions)
     if constexpr (SCALE) {
         if (K == 8) {
-            hipLaunchKernelGGL((dispatch_kernel<F32, SCALE, 8, VB, IDENT>), grid, dim3(256), 0, s, dest, src, scale, recv, ntok, K, rowvec, nrows);
+            if (full) hipLaunchKernelGGL((dispatch_kernel<F32, SCALE, 8, VB, IDENT, true>), grid, dim3(256), 0, s, dest, src, scale, recv, ntok, K, rowvec, nrows);
+            else hipLaunchKernelGGL((dispatch_kernel<F32, SCALE, 8, VB, IDENT, false>), grid, dim3(256), 0, s, dest, src, scale, recv, ntok, K, rowvec, nrows);
             return;
         }
     }
-    hipLaunchKernelGGL((dispatch_kernel<F32, SCALE, 0, VB, IDENT>), grid, dim3(256), 0, s, dest, src, scale, recv, ntok, K, rowvec, nrows);
+    if (full) hipLaunchKernelGGL((dispatch_kernel<F32, SCALE, 0, VB, IDENT, true>), grid, dim3(256), 0, s, dest, src, scale, recv, ntok, K, rowvec, nrows);
+    else hipLaunchKernelGGL((dispatch_kernel<F32, SCALE, 0, VB, IDENT, false>), grid, dim3(256), 0, s, dest, src, scale, recv, ntok, K, rowvec, nrows);
 }
 
 template <bool F32, bool GATES, bool IDENT = false>
 static void launch_combine(int K, dim3 grid, hipStream_t s, const int32_t* dest, const uint4* y,
                            const float* gates, uint4* out, int ntok, int rowvec, long long nrows) {
-    hipLaunchKernelGGL((combine_kernel<F32, GATES, MOONEP_COMBINE_VB, IDENT>), grid, dim3(256), 0, s, dest, y, gates, out, ntok, K, rowvec, nrows);
+    // the full-row form measured 2% faster with gates and 2% slower with unit weights
+    if (GATES && rowvec % (64 * MOONEP_COMBINE_VB) == 0)
+        hipLaunchKernelGGL((combine_kernel<F32, GATES, MOONEP_COMBINE_VB, IDENT, true>), grid, dim3(256), 0, s, dest, y, gates, out, ntok, K, rowvec, nrows);
+    else
+        hipLaunchKernelGGL((combine_kernel<F32, GATES, MOONEP_COMBINE_VB, IDENT, false>), grid, dim3(256), 0, s, dest, y, gates, out, ntok, K, rowvec, nrows);
 }
 
 // The sort-copy of the staged baseline, one wave per row p, 16-byte vectors per lane:

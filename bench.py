@@ -34,16 +34,16 @@ SWEEP = (0.0, 0.5, 2.0, 4.0, 8.0)
 # one-wave counter reset before their GEMM, the row GEMM calls a one-wave tile prefix.
 KERNEL_NAMES = {
     "prefetch": "moonep::prefetch_kernel",
-    "dispatch": "moonep::dispatch_kernel<false, false, 0, 2, false>",
+    "dispatch": "moonep::dispatch_kernel<false, false, 0, 2, false, true>",
     "gemm_gate_up": "moonep::gemm_rows_kernel<0, 0, 4>",
     "gemm_down": "moonep::gemm_rows_kernel<0, 1, 4>",
-    "combine": "moonep::combine_kernel<false, true, 7, false>",
-    "dispatch_bwd": "moonep::dispatch_kernel<false, true, 8, 2, false>",
+    "combine": "moonep::combine_kernel<false, true, 7, false, true>",
+    "dispatch_bwd": "moonep::dispatch_kernel<false, true, 8, 2, false, true>",
     "gemm_dact": "moonep::gemm_rows_kernel<1, 2, 4>",
     "gemm_dx": "moonep::gemm_rows_kernel<1, 1, 4>",
     "gemm_dw2": "moonep::gemm_dw_kernel<4, 2>",
     "gemm_dw13": "moonep::gemm_dw_kernel<4, 13>",
-    "combine_bwd": "moonep::combine_kernel<false, false, 7, false>",
+    "combine_bwd": "moonep::combine_kernel<false, false, 7, false, false>",
     "reduce_grad": "moonep::reduce_grad_kernel",
 }
 # sources each kernel is compiled from (a code change to any of them, comments aside, voids its
