@@ -19,7 +19,9 @@
 //     per-lane offset.  Row kernels: 64-k stages in five 32 KiB buffers, one operand
 //     triple-buffered (loaded two stages ahead), the other double-buffered.  Weight-gradient
 //     kernel: a ring of four 32-k stages loaded three steps ahead.  One explicit vmcnt wait
-//     and one barrier per stage.
+//     and one barrier per stage.  The steady-state stages take their "does a later stage
+//     exist" conditions as compile-time flags (the last stages are peeled off), so they carry
+//     no branch around their copies and waits.
 //   * LDS tiles are XOR-swizzled in 16-byte chunks so fragment reads are bank-conflict
 //     free.  k-contiguous operands (activations, backward weights) are read with
 //     ds_read_b128; m/n-contiguous operands (forward weights, both dW operands) stay
@@ -35,8 +37,8 @@
 //     segment's end load from a zero block kept in the plan workspace.
 //   * Epilogues are fused and staged through LDS for 16-byte stores: SwiGLU (act =
 //     silu(gate) * up, Gt|U saved) after the gate/up GEMM; SwiGLU' (dGt, dU written over
-//     the saved Gt|U) after dA = dY W2^T; fp32 store or accumulate into the home or
-//     reduce-buffer gradient for dW.
+//     the saved Gt|U, which arrives by LDS DMA ahead of each quarter) after dA = dY W2^T;
+//     fp32 store or accumulate into the home or reduce-buffer gradient for dW.
 #include <type_traits>
 
 #include "common.h"
