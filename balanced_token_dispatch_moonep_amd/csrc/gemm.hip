@@ -56,9 +56,8 @@ constexpr int BM = 256, BN = 256, BK = 32, NSTAGE = 4;
 constexpr int OP_BYTES = 256 * BK * 2;             // one operand tile of one stage: 16 KiB
 constexpr int STAGE_BYTES = 2 * OP_BYTES;
 constexpr int GEMM_SMEM = NSTAGE * STAGE_BYTES;    // 128 KiB
-// weight-gradient kernel: float4 stores per wave and tile (8 waves of 128x64), and the start of
-// its epilogue staging (ring buffer 3 onwards, clear of the next tile's first three steps)
-constexpr int DW_STORES = 32;
+// weight-gradient kernel: the start of its epilogue staging (ring buffer 3 onwards, clear of the
+// next tile's first three steps)
 constexpr int DW_STG = 3 * STAGE_BYTES;
 // Row kernels: K step 64, so every k-contiguous row segment a DMA lane group fetches is one full
 // 128-byte line.
@@ -274,39 +273,29 @@ __device__ __forceinline__ void dw_prologue(int nst, Issue&& issue) {
             for (int p = 0; p < WL<WN>::PARTS; ++p) issue(s, s, p);
 }
 
-// vmcnt retires this wave's vector memory operations in issue order, so "at most n outstanding"
-// means all but the last n issued have completed.  ns: at least DW_STORES vector memory
-// operations (the previous tile's epilogue stores) were issued between dw_prologue and this call;
-// the waits then let those stores drain while steps 0 and 1 run.
-template <int N>
-__device__ __forceinline__ void wait_vm_ns(bool ns) {
-    if (ns) wait_vm<N + DW_STORES>();
-    else wait_vm<N>();
-}
-
 // Fragments are double-buffered in registers: the reads of the next slice are issued before the
 // MFMAs of the current one; the step barrier sits between a step's two slices so the MFMAs already
 // issued keep the matrix cores busy across it; and the DMA loads of step s+3 are spread between the
 // MFMAs of the second slice, so no burst of memory instructions stalls the wave's in-order issue
 // while the matrix pipe drains.
 template <int WN, typename Issue, typename IssueFast, typename FastRun>
-__device__ __forceinline__ void dw_main(f32x16_t (&acc)[4][WL<WN>::TN], char* smem, int nst, bool ns, int wm,
+__device__ __forceinline__ void dw_main(f32x16_t (&acc)[4][WL<WN>::TN], char* smem, int nst, int wm,
                                         int wn, int lane, Issue&& issue, IssueFast&& issue_fast,
                                         FastRun&& fast_run) {
     using L = WL<WN>;
     constexpr int PER = L::PER_STEP;
     if (nst > 0) {
-        // step 0 landed; after it come steps 1 and 2 (if any) and the counted stores
-        if (nst >= 3) wait_vm_ns<2 * PER>(ns);
-        else if (nst == 2) wait_vm_ns<PER>(ns);
-        else wait_vm_ns<0>(ns);
+        // step 0 landed (vmcnt retires in issue order: all but the last n issued are done);
+        // steps 1 and 2 (if any) may still be in flight
+        if (nst >= 3) wait_vm<2 * PER>();
+        else if (nst == 2) wait_vm<PER>();
+        else wait_vm<0>();
         block_sync();
         Frags<L::TN> f0, f1;
         load_frags<WN>(f0, smem, 0, wm, wn, lane);
-        // One step.  FAST: a step s in 2 .. nst-4 (step s+3 exists and the counted stores have
-        // retired from the waits) whose step s+3 is full and does not end its segment; the
-        // conditions are then compile-time, so these steps carry no branch around their waits and
-        // copies.
+        // One step.  FAST: a step s in 2 .. nst-4 (step s+3 exists) whose step s+3 is full and
+        // does not end its segment; the conditions are then compile-time, so these steps carry no
+        // branch around their waits and copies.
         auto step = [&](int s, auto fast_c) {
             constexpr bool fast = decltype(fast_c)::value;
             const char* st = smem + (s & (NSTAGE - 1)) * STAGE_BYTES;
@@ -319,15 +308,9 @@ __device__ __forceinline__ void dw_main(f32x16_t (&acc)[4][WL<WN>::TN], char* sm
             __builtin_amdgcn_sched_barrier(0);
             wait_lgkm0();
             if (fast || s + 1 < nst) {
-                // step s+1 must have landed: step s+2 may still be in flight, and during steps 0
-                // and 1 the counted stores (issued after step 2) as well
-                if constexpr (fast) {
-                    wait_vm<PER>();
-                } else {
-                    const bool early = ns && s <= 1;
-                    if (s + 2 < nst) wait_vm_ns<PER>(early);
-                    else wait_vm_ns<0>(early);
-                }
+                // step s+1 must have landed; step s+2 may still be in flight
+                if (fast || s + 2 < nst) wait_vm<PER>();
+                else wait_vm<0>();
                 block_sync();
                 load_frags<WN>(f0, smem + ((s + 1) & (NSTAGE - 1)) * STAGE_BYTES, 0, wm, wn, lane);
             }
@@ -834,11 +817,12 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_rows_kernel(GemmArgs a) {
 //
 // The persistent loop is software-pipelined by one tile: after tile i's main loop, the workgroup
 // sets up tile i+1 (its id was fetched during tile i) and issues its first three steps, then
-// stages and stores tile i's result.  Tile i+1's first two waits leave room for those stores to
-// drain while its first steps run.  In the compiled kernel most of them drain earlier: the
-// compiler waits for all of a wave's memory operations after the tile counter's atomic add
-// (wave 0) and before each epilogue slice (a side effect of the accumulate path's loads).  That
-// pacing measured 1-2% faster than every variant without those waits, so it is kept.
+// stages and stores tile i's result, so tile i+1's first copies are in flight during the
+// epilogue.  Every wave then waits for all of its stores before tile i+1's main loop.  Letting
+// the stores drain behind tile i+1's first steps instead measured no faster, and variants that
+// issued all of them without pacing measured 1-2% slower; the compiled epilogue also waits for
+// the previous slice's stores before each slice (a side effect of the accumulate path's loads),
+// and wave 0 for all of its operations after the tile counter's atomic add.
 template <int WN>
 constexpr int dw_smem() { return DW_STG + WL<WN>::WAVES * 16 * WL<WN>::EPL * 4; }
 static_assert(dw_smem<2>() <= ROWS_SMEM - 4096 && dw_smem<4>() <= ROWS_SMEM - 4096,
@@ -847,7 +831,6 @@ static_assert(dw_smem<2>() <= ROWS_SMEM - 4096 && dw_smem<4>() <= ROWS_SMEM - 40
 template <int WN, int WHICH>
 __global__ __launch_bounds__(128 * WN, 1) void gemm_dw_kernel(GemmArgs a) {
     using L = WL<WN>;
-    constexpr bool kCounted = 256 / L::WAVES == DW_STORES;   // stores per wave fit the vmcnt waits
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     __shared__ Segment s_seg[2][kMaxR + 1];
     __shared__ int s_tile[2];
@@ -978,14 +961,13 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_dw_kernel(GemmArgs a) {
         start_issue(0);
         dw_prologue<WN>(nst, issue);
     }
-    bool ns = false;   // DW_STORES stores were issued after this tile's first copies
     while (have) {
         int nxt = 0;
         if (tid == 0) nxt = atomicAdd(a.counter, 1);   // consumed after the main loop (an atomic
                                                        // add on purpose: see the loop's header)
         f32x16_t acc[4][L::TN];
         zero_acc<L::TN>(acc);
-        dw_main<WN>(acc, smem, nst, ns, wm, wn, lane, issue, issue_fast, fast_run);
+        dw_main<WN>(acc, smem, nst, wm, wn, lane, issue, issue_fast, fast_run);
         // this tile's output, kept while the next tile is set up
         float* const cout = out;
         const int cm0 = m0, cn0 = n0;
@@ -997,11 +979,11 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_dw_kernel(GemmArgs a) {
             start_issue(par ^ 1);
             dw_prologue<WN>(nst, issue);
         }
-        // this tile's stores; an interior tile issues exactly DW_STORES per wave
-        const bool full = kCounted && cm0 + BM <= a.M && cn0 + BN <= a.N;
+        // this tile's stores (unmasked for an interior tile), all retired before the next tile
+        const bool full = cm0 + BM <= a.M && cn0 + BN <= a.N;
         if (full) epi_dw<WN, true>(a, acc, ep, wm, wn, lane, cout, cm0, cn0);
         else epi_dw<WN, false>(a, acc, ep, wm, wn, lane, cout, cm0, cn0);
-        ns = full;
+        wait_vm<0>();
         have = next;
         par ^= 1;
     }
