@@ -295,7 +295,8 @@ __device__ __forceinline__ void dw_main(f32x16_t (&acc)[4][WL<WN>::TN], char* sm
         load_frags<WN>(f0, smem, 0, wm, wn, lane);
         // One step.  FAST: a step s in 2 .. nst-4 (step s+3 exists) whose step s+3 is full and
         // does not end its segment; the conditions are then compile-time, so these steps carry no
-        // branch around their waits and copies.
+        // branch around their waits and copies.  (Steps 0 and 1 run the general way: starting
+        // the fast run at step 0 measured the same.)
         auto step = [&](int s, auto fast_c) {
             constexpr bool fast = decltype(fast_c)::value;
             const char* st = smem + (s & (NSTAGE - 1)) * STAGE_BYTES;
