@@ -101,6 +101,26 @@ def test_backward_mid(B):
     _backward_check(MID.with_(B=B))
 
 
+def _random_cfgs(n=4, seed=11):
+    """Seeded random small layers: rank counts, slots (including none, so fallback targets with
+    several row segments), top-k, ragged H and I, and skew all vary."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        R = int(rng.choice([2, 4, 8]))
+        E = R * int(rng.choice([2, 4]))
+        out.append(MID.with_(R=R, E=E, B=int(rng.choice([0, 1, 2, 4])),
+                             K=int(rng.integers(1, min(E, 4) + 1)), S=int(rng.choice([96, 200, 333, 512])),
+                             H=int(rng.choice([256, 320, 576])), I=int(rng.choice([128, 192, 320])),
+                             lam=round(float(rng.uniform(0.0, 2.0)), 3), seed=100 + i))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _random_cfgs(), ids=lambda c: f"R{c.R}E{c.E}B{c.B}K{c.K}S{c.S}H{c.H}I{c.I}")
+def test_backward_random_shapes(cfg):
+    _backward_check(cfg)
+
+
 def _backward_check(cfg):
     B = cfg.B
     topk, gates, xb, wb13, wb2, d, plan, dest, layer = _setup(cfg, training=True)
