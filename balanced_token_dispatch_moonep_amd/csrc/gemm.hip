@@ -705,8 +705,10 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_rows_kernel(GemmArgs a) {
     // tiles take different times.  Tile ids pass through two words at the start of the fifth
     // operand buffer, alternating: between a tile's last barrier and the next tile's first one no
     // copy targets that buffer (the first copies go to the first stage's buffers and the deep
-    // operand's second stage), and the epilogue staging ends below it.  All 160 KiB of LDS are
-    // dynamic, so no static LDS is left for them.
+    // operand's second stage), and the epilogue staging ends below it.  The dA epilogue's Gt|U
+    // copies do land there, but each is awaited before that epilogue's last barrier, and a word
+    // is read only after thread 0 rewrites it.  All 160 KiB of LDS are dynamic, so no static LDS
+    // is left for them.
     int* const s_t = reinterpret_cast<int*>(smem + 4 * OP2_BYTES);
     int fs = 0;
     auto publish = [&](int v) {
