@@ -54,6 +54,9 @@ KERNEL_SOURCES = {
     "dispatch_bwd": ("permute.hip",), "combine_bwd": ("permute.hip",),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_busy.json")
+SIMDS = 256 * 4      # MI355X: 256 compute units of 4 SIMDs
+XCDS = 8
 
 
 def parse():
@@ -70,6 +73,11 @@ def parse():
                    help="no GPU work: reduce two rocprofv3 --pmc runs of this bench (FETCH_SIZE, then "
                         "WRITE_SIZE) and that run's JSON line to per-launch HBM bytes; writes "
                         "profiles/hbm_traffic.json and prints a markdown summary")
+    p.add_argument("--mfma-from", nargs=2, metavar=("PMC_DIR", "BENCH_JSON"),
+                   help="no GPU work: reduce a rocprofv3 --pmc run of this bench (SQ_VALU_MFMA_BUSY_CYCLES, "
+                        "SQ_INSTS_VALU_MFMA_MOPS_BF16, GRBM_GUI_ACTIVE, with --kernel-trace) and that run's "
+                        "JSON line to per-kernel matrix-core busy fractions; writes profiles/mfma_busy.json "
+                        "and prints a markdown summary")
     p.add_argument("--stats-from", metavar="DIR",
                    help="no GPU work: print a markdown table of a rocprofv3 --stats kernel summary")
     return p.parse_args()
@@ -112,6 +120,8 @@ def main():
         return write_traffic(*args.traffic_from)
     if args.stats_from:
         return print_stats(args.stats_from)
+    if args.mfma_from:
+        return write_mfma(*args.mfma_from)
     if args.steps < 1 or args.warmup < 0:
         print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
         return 2
@@ -215,6 +225,10 @@ def main():
     roofline = {"bound": r["bound"], "achieved": r["achieved"], "peak": r["peak"], "unit": r["unit"],
                 "frac": r["frac"], "traffic": traffic_of(dom, work[dom][2]), "kernel": KERNEL_NAMES[dom],
                 "call": dom, "ms": r["ms"], "per_launch": work[dom][3]}
+    if r["bound"] == "mfma":
+        roofline["mfma_busy"] = stored_of(MFMA_FILE, dom, "mfma_busy_frac")
+    for k in gemm_keys:
+        rooflines[k]["mfma_busy"] = stored_of(MFMA_FILE, k, "mfma_busy_frac")
 
     # ---- maxvio sweep (same shapes): the whole training step per maxvio ----------------------
     sweep = []
@@ -496,6 +510,19 @@ def _sources_digest(call):
     return h.hexdigest()[:16]
 
 
+def stored_of(path, call, field):
+    """A per-call figure stored by a counter reducer, or None when none is stored for the
+    call's kernel as it is now built (digest of its sources, comments excluded)."""
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(call)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("sources") != _sources_digest(call):
+        return None
+    return rec.get(field)
+
+
 def traffic_of(call, algorithmic_bytes):
     """HBM bytes per launch of the call's kernel from the stored rocprofv3 FETCH_SIZE / WRITE_SIZE
     counts (scaled by a copy kernel of known size), or None when none are stored for the kernel
@@ -580,6 +607,69 @@ def write_traffic(fetch_dir, write_dir, bench_json):
           f"FETCH_SIZE x {kf:.4f}, WRITE_SIZE x {kw:.4f}.\n")
     print("| kernel | call | fetch GB | write GB | HBM GB / launch | algorithmic GB | ratio |")
     print("|---|---|---:|---:|---:|---:|---:|")
+    print("\n".join(rows))
+    return 0
+
+
+def _kernel_durations(d):
+    """Mean duration (ns) per kernel name from a rocprofv3 kernel_trace.csv tree."""
+    import csv
+    import glob
+    per = {}
+    for f in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                per.setdefault(row["Kernel_Name"], []).append(
+                    int(row["End_Timestamp"]) - int(row["Start_Timestamp"]))
+    return {k: sum(v) / len(v) for k, v in per.items()}
+
+
+def write_mfma(pmc_dir, bench_json):
+    """Matrix-core busy fraction of every timed GEMM kernel.
+
+    SQ_VALU_MFMA_BUSY_CYCLES is counted per SIMD and GRBM_GUI_ACTIVE per XCD; rocprofv3 sums
+    each over its instances.  busy = MFMA busy cycles / (GUI-active cycles of one XCD x 1024
+    SIMDs).  SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 is the bf16 flops the matrix cores executed
+    (padding included).  The implied shader clock is one XCD's GUI-active cycles over the
+    kernel's traced duration."""
+    with open(bench_json) as f:
+        line = [ln for ln in f if ln.startswith("{")][-1]
+    run = json.loads(line)
+    busy = _pmc_per_dispatch(pmc_dir, "SQ_VALU_MFMA_BUSY_CYCLES")
+    mops = _pmc_per_dispatch(pmc_dir, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    grbm = _pmc_per_dispatch(pmc_dir, "GRBM_GUI_ACTIVE")
+    dur = _kernel_durations(pmc_dir)
+    out = {"_method": {"busy": "sum SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs)",
+                       "executed_flops": "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512",
+                       "clock": "GRBM_GUI_ACTIVE / 8 / traced duration", "workload": run["config"]}}
+    rows = []
+    for c, kname in KERNEL_NAMES.items():
+        if not c.startswith("gemm_"):
+            continue
+        k = next((n for n in busy if _kernel_call(n) == c), None)
+        if k is None or k not in grbm:
+            continue
+        cyc = grbm[k][0] / XCDS
+        frac = busy[k][0] / (cyc * SIMDS)
+        exe = mops.get(k, (0.0, 0))[0] * 512.0
+        alg = run["rooflines"].get(c, {}).get("flops")
+        ns = dur.get(k)
+        ghz = cyc / ns if ns else None
+        out[c] = {"kernel": kname, "mfma_busy_frac": round(frac, 4), "gui_cycles": round(cyc),
+                  "executed_flops": exe, "algorithmic_flops": alg,
+                  "executed_over_algorithmic": round(exe / alg, 4) if alg else None,
+                  "traced_ms": round(ns / 1e6, 4) if ns else None,
+                  "clock_GHz": round(ghz, 3) if ghz else None,
+                  "sources": _sources_digest(c), "dispatches": busy[k][1]}
+        rows.append(f"| `{kname}` | {c} | {frac:.3f} | {exe / 1e12:.2f} | "
+                    + (f"{alg / 1e12:.2f} | {exe / alg:.3f} | " if alg else "— | — | ")
+                    + (f"{ns / 1e6:.2f} | {ghz:.2f} |" if ns else "— | — |"))
+    with open(MFMA_FILE, "w") as f:
+        json.dump(out, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print("| kernel | call | MFMA busy | executed TFLOP | algorithmic TFLOP | executed / algorithmic | "
+          "traced ms | implied clock GHz |")
+    print("|---|---|---:|---:|---:|---:|---:|---:|")
     print("\n".join(rows))
     return 0
 

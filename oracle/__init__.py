@@ -20,7 +20,8 @@ from .plan import (RoutingError, CapacityError, Plan, validate_routing, expert_c
                    maxvio, make_plan, destinations, stats_vector, STAT_NAMES,
                    ST_BAD_ID, ST_DUP_ID, ST_CAPACITY, ST_OVERFLOW, ST_TRAIN_FALLBACK)
 from .layer import (dispatch, combine, groups, prefetch, ffn_forward, ffn_backward,
-                    reduce_grad, moe_direct, moe_direct_backward, silu)
+                    reduce_grad, moe_direct, moe_direct_backward, silu, swiglu_ffn,
+                    swiglu_ffn_backward, expert_grad_direct, token_grad_direct)
 from .brute import min_replicas_milp, min_replicas_enum, plan_is_feasible_flow
 from .memory import buffer_bytes
 
@@ -29,6 +30,7 @@ __all__ = [
     "make_plan", "destinations", "stats_vector", "STAT_NAMES", "ST_BAD_ID", "ST_DUP_ID",
     "ST_CAPACITY", "ST_OVERFLOW", "ST_TRAIN_FALLBACK", "dispatch", "combine", "groups",
     "prefetch", "ffn_forward", "ffn_backward", "reduce_grad", "moe_direct",
-    "moe_direct_backward", "silu", "min_replicas_milp", "min_replicas_enum",
+    "moe_direct_backward", "silu", "swiglu_ffn", "swiglu_ffn_backward", "expert_grad_direct",
+    "token_grad_direct", "min_replicas_milp", "min_replicas_enum",
     "plan_is_feasible_flow", "buffer_bytes",
 ]

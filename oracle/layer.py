@@ -24,7 +24,7 @@ def _f64(a: np.ndarray) -> np.ndarray:
     a = np.asarray(a)
     if a.dtype == np.uint16:                       # bf16 bit patterns
         return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    return a.astype(np.float64)
+    return np.asarray(a, dtype=np.float64)
 
 
 def silu(x: np.ndarray) -> np.ndarray:
@@ -139,6 +139,33 @@ def _weights(plan: Plan, q: int, w: int, w13, w2, s13, s2):
 # expert FFN over groups
 # ----------------------------------------------------------------------------
 
+def swiglu_ffn(X: np.ndarray, W13: np.ndarray, W2: np.ndarray):
+    """One expert's SwiGLU FFN on rows X, float64: Gt = X W1, U = X W3 (W13 = [W1 | W3]),
+    A = silu(Gt) * U, Y = A W2 [TC, flowchart "Group GEMM"; TC, What we measured, Table 2:
+    three projections].  bf16 inputs arrive as uint16 bit patterns and are widened exactly.
+    Returns (gu = [Gt | U], A, Y)."""
+    X, W13, W2 = _f64(X), _f64(W13), _f64(W2)
+    I = W2.shape[0]
+    g = X @ W13
+    a = silu(g[:, :I]) * g[:, I:]
+    return g, a, a @ W2
+
+
+def swiglu_ffn_backward(X: np.ndarray, gu: np.ndarray, act: np.ndarray, dY: np.ndarray,
+                        W13: np.ndarray, W2: np.ndarray):
+    """Backward of ``swiglu_ffn`` for upstream dY, float64.
+
+    dA = dY W2^T; dGt = dA * U * sig(Gt) * (1 + Gt (1 - sig(Gt))); dU = dA * silu(Gt);
+    dX = [dGt dU] W13^T; dW13 = X^T [dGt dU]; dW2 = A^T dY.
+    Returns (dgu = [dGt | dU], dX, dW13, dW2)."""
+    I = W2.shape[0]
+    gt, u = gu[:, :I], gu[:, I:]
+    da = dY @ W2.T
+    sg = _sigmoid(gt)
+    dgu = np.concatenate([da * u * sg * (1.0 + gt * (1.0 - sg)), da * silu(gt)], axis=1)
+    return dgu, dgu @ W13.T, X.T @ dgu, act.T @ dY
+
+
 def ffn_forward(plan: Plan, recv, w13, w2, s13, s2):
     """Grouped SwiGLU FFN on the receive buffer, group by group.
 
@@ -154,12 +181,8 @@ def ffn_forward(plan: Plan, recv, w13, w2, s13, s2):
     y = np.zeros((M, H))
     for (q, w, row0, rows, kind, idx) in groups(plan):
         W13, W2 = _weights(plan, q, w, w13, w2, s13, s2)
-        xg = X[row0:row0 + rows]
-        g = xg @ W13
-        a = silu(g[:, :I]) * g[:, I:]
-        gu[row0:row0 + rows] = g
-        act[row0:row0 + rows] = a
-        y[row0:row0 + rows] = a @ W2
+        sl = slice(row0, row0 + rows)
+        gu[sl], act[sl], y[sl] = swiglu_ffn(X[sl], W13, W2)
     return gu, act, y
 
 
@@ -198,15 +221,7 @@ def ffn_backward(plan: Plan, recv, gu, act, dy, w13, w2, s13, s2):
     for (q, w, row0, rows, kind, idx) in order:
         W13, W2 = _weights(plan, q, w, w13, w2, s13, s2)
         sl = slice(row0, row0 + rows)
-        gt, u = GU[sl, :I], GU[sl, I:]
-        da = DY[sl] @ W2.T
-        sg = _sigmoid(gt)
-        dgt = da * u * sg * (1.0 + gt * (1.0 - sg))
-        du = da * silu(gt)
-        dgu = np.concatenate([dgt, du], axis=1)
-        drecv[sl] = dgu @ W13.T
-        g2 = A[sl].T @ DY[sl]
-        g13 = X[sl].T @ dgu
+        _, drecv[sl], g13, g2 = swiglu_ffn_backward(X[sl], GU[sl], A[sl], DY[sl], W13, W2)
         if kind == "slot":
             rb13[q, idx] += g13
             rb2[q, idx] += g2
@@ -239,20 +254,33 @@ def moe_direct(x, topk, gates, w13, w2) -> np.ndarray:
     """out[r,s] = sum_k gates[r,s,k] * FFN_{topk[r,s,k]}(x[r,s]), float64, no plan involved."""
     xf = _f64(x)
     R, S, H = xf.shape
-    K = topk.shape[2]
     E = w13.shape[0]
-    I = w2.shape[1]
     out = np.zeros((R, S, H))
     for e in range(E):
         r_i, s_i, k_i = np.nonzero(topk == e)
         if r_i.size == 0:
             continue
-        W13, W2 = _f64(w13[e]), _f64(w2[e])
-        xe = xf[r_i, s_i]
-        g = xe @ W13
-        ye = (silu(g[:, :I]) * g[:, I:]) @ W2
+        _, _, ye = swiglu_ffn(xf[r_i, s_i], _f64(w13[e]), _f64(w2[e]))
         np.add.at(out, (r_i, s_i), np.asarray(gates, np.float64)[r_i, s_i, k_i][:, None] * ye)
     return out
+
+
+def expert_grad_direct(x, topk, gates, dout, e: int, W13, W2):
+    """Plan-free gradient of expert e's weights: every (token, k) routed to e contributes,
+    whichever rank serves it, with upstream gradient gates[r,s,k] * dOut[r,s] (float64).
+
+    ``W13`` [H, 2I] and ``W2`` [I, H] are expert e's weights.  Returns (dW13_e, dW2_e, rows of
+    dx contributed by e as (r_i, s_i, dx_rows))."""
+    xf = _f64(x)
+    r_i, s_i, k_i = np.nonzero(topk == e)
+    W13f, W2f = _f64(W13), _f64(W2)
+    if r_i.size == 0:
+        return (np.zeros(W13f.shape), np.zeros(W2f.shape), (r_i, s_i, np.zeros((0, xf.shape[-1]))))
+    xe = xf[r_i, s_i]
+    gu, a, _ = swiglu_ffn(xe, W13f, W2f)
+    dy = np.asarray(gates, np.float64)[r_i, s_i, k_i][:, None] * _f64(dout[r_i, s_i])
+    _, dxe, dW13, dW2 = swiglu_ffn_backward(xe, gu, a, dy, W13f, W2f)
+    return dW13, dW2, (r_i, s_i, dxe)
 
 
 def moe_direct_backward(x, topk, gates, w13, w2, dout, experts=None):
@@ -261,28 +289,33 @@ def moe_direct_backward(x, topk, gates, w13, w2, dout, experts=None):
     ``experts`` restricts the computation to those experts (dx then only holds their share).
     """
     xf = _f64(x)
-    do = _f64(dout)
-    R, S, H = xf.shape
     E = w13.shape[0]
-    I = w2.shape[1]
     dx = np.zeros_like(xf)
-    dW13 = np.zeros((E, H, 2 * I))
-    dW2 = np.zeros((E, I, H))
-    gf = np.asarray(gates, np.float64)
+    dW13 = np.zeros((E,) + tuple(w13.shape[1:]))
+    dW2 = np.zeros((E,) + tuple(w2.shape[1:]))
     for e in (range(E) if experts is None else experts):
-        r_i, s_i, k_i = np.nonzero(topk == e)
-        if r_i.size == 0:
-            continue
-        W13, W2 = _f64(w13[e]), _f64(w2[e])
-        xe = xf[r_i, s_i]
-        g = xe @ W13
-        gt, u = g[:, :I], g[:, I:]
-        a = silu(gt) * u
-        dy = gf[r_i, s_i, k_i][:, None] * do[r_i, s_i]
-        da = dy @ W2.T
-        sg = _sigmoid(gt)
-        dgu = np.concatenate([da * u * sg * (1.0 + gt * (1.0 - sg)), da * silu(gt)], axis=1)
-        np.add.at(dx, (r_i, s_i), dgu @ W13.T)
-        dW13[e] = xe.T @ dgu
-        dW2[e] = a.T @ dy
+        dW13[e], dW2[e], (r_i, s_i, dxe) = expert_grad_direct(xf, topk, gates, dout, e, w13[e], w2[e])
+        np.add.at(dx, (r_i, s_i), dxe)
     return dx, dW13, dW2
+
+
+def token_grad_direct(x, topk, gates, dout, tokens, weights_of):
+    """Plan-free output and input gradient of a few tokens: for each (r, s) in ``tokens``,
+    out[r,s] = sum_k g_k FFN_{e_k}(x[r,s]) and dx[r,s] = sum_k of the gradient of g_k FFN_{e_k}
+    at x[r,s] for upstream dOut[r,s], both in k order (float64).  ``weights_of(e)`` returns
+    expert e's (W13 [H, 2I], W2 [I, H]), so only the experts of these tokens are read.
+    Returns (out [n, H], dx [n, H])."""
+    xf = _f64(np.asarray([x[r, s] for (r, s) in tokens]))
+    do = _f64(np.asarray([dout[r, s] for (r, s) in tokens]))
+    out = np.zeros(xf.shape)
+    dx = np.zeros(xf.shape)
+    for i, (r, s) in enumerate(tokens):
+        for k in range(topk.shape[2]):
+            W13, W2 = (_f64(w) for w in weights_of(int(topk[r, s, k])))
+            g = float(gates[r, s, k])
+            xi = xf[i:i + 1]
+            gu, a, y = swiglu_ffn(xi, W13, W2)
+            out[i] += g * y[0]
+            _, dxi, _, _ = swiglu_ffn_backward(xi, gu, a, g * do[i:i + 1], W13, W2)
+            dx[i] += dxi[0]
+    return out, dx

@@ -325,12 +325,9 @@ def test_full_layer_forward_sampled(B):
         e = w if w < cfg.E else next(en.e for en in plan.entries if en.q == q and en.w == w)
         W13, W2 = _expert_np(layer.w13[e]), _expert_np(layer.w2[e])
         sel = row0 + rng.choice(rows, size=min(rows, 8), replace=False)
-        X = O.layer._f64(xb.reshape(-1, cfg.H)[src_tok[sel]])
         assert np.array_equal(bits_of(layer.recv[torch.as_tensor(sel, device=DEV)]),
                               xb.reshape(-1, cfg.H)[src_tok[sel]])
-        g = X @ W13
-        a = O.silu(g[:, :cfg.I]) * g[:, cfg.I:]
-        yref = a @ W2
+        _, _, yref = O.swiglu_ffn(xb.reshape(-1, cfg.H)[src_tok[sel]], W13, W2)
         got = f64_of(layer.y[torch.as_tensor(sel, device=DEV)])
         err = max_row_rel(got, yref)
         say(f"  {kind} group q={q} w={w} e={e} rows={rows}: y max row rel {err:.3e}")
@@ -339,12 +336,13 @@ def test_full_layer_forward_sampled(B):
 
 def test_full_layer_backward_experts():
     """Training at maxvio 8 with B=4: full dW of a fallback expert, a slot-replicated expert
-    and a plain expert after reduce_grad, against the plan-free gradient."""
+    and a plain expert after reduce_grad, against the plan-free gradient; and the output and
+    input gradient of sampled tokens (the unit-weight combine of the timed backward)."""
     cfg = W.CONFIGS["train"].with_(maxvio=8.0)
     topk, gates, xb, plan, dest, layer = _full_layer(cfg, cfg.B, True)
     doutb = W.grad_rows(cfg.R, cfg.S, cfg.H, cfg.seed, "bf16")
-    layer.forward(bf16_from_bits(xb), i32(topk), f32(gates))
-    layer.backward(bf16_from_bits(doutb), f32(gates))
+    out = layer.forward(bf16_from_bits(xb), i32(topk), f32(gates)).clone()
+    dx = layer.backward(bf16_from_bits(doutb), f32(gates))
     torch.cuda.synchronize()
     fb = sorted({en.e for en in plan.entries if en.w < cfg.E})
     sl = sorted({en.e for en in plan.entries if en.w >= cfg.E} - set(fb))
@@ -355,29 +353,39 @@ def test_full_layer_backward_experts():
     for e in chosen:
         W13 = layer.w13[e].cpu().view(torch.int16).numpy().view(np.uint16)
         W2 = layer.w2[e].cpu().view(torch.int16).numpy().view(np.uint16)
-        # the plan-free gradient of expert e: every (token, k) routed to e, whatever rank serves it
-        r_i, s_i, k_i = np.nonzero(topk == e)
-        xe = O.layer._f64(xb[r_i, s_i])
-        g = xe @ O.layer._f64(W13)
-        gt, u = g[:, :cfg.I], g[:, cfg.I:]
-        a = O.silu(gt) * u
-        dy = np.asarray(gates, np.float64)[r_i, s_i, k_i][:, None] * O.layer._f64(doutb[r_i, s_i])
-        da = dy @ O.layer._f64(W2).T
-        sg = 1.0 / (1.0 + np.exp(-gt))
-        dgu = np.concatenate([da * u * sg * (1.0 + gt * (1.0 - sg)), da * O.silu(gt)], axis=1)
-        ref13 = xe.T @ dgu
-        ref2 = a.T @ dy
+        # every (token, k) routed to e, whatever rank serves it
+        ref13, ref2, _ = O.expert_grad_direct(xb, topk, gates, doutb, e, W13, W2)
         e13 = rel_fro(f64_of(layer.dw13[e]), ref13)
         e2 = rel_fro(f64_of(layer.dw2[e]), ref2)
         say(f"  expert {e} (L={plan.L[e]}): dW13 {e13:.3e} dW2 {e2:.3e}")
         assert e13 <= TOL and e2 <= TOL
     assert not layer.dw13_red.any() and not layer.dw2_red.any()
+    # sampled tokens: out and dx rows (each sums K expert rows of y / drecv at full H)
+    rng = np.random.default_rng(4)
+    toks = [(int(r), int(s)) for r, s in zip(rng.integers(0, cfg.R, 4), rng.integers(0, cfg.S, 4))]
+    cache = {}
+
+    def weights_of(e):
+        if e not in cache:
+            cache[e] = (layer.w13[e].cpu().view(torch.int16).numpy().view(np.uint16),
+                        layer.w2[e].cpu().view(torch.int16).numpy().view(np.uint16))
+        return cache[e]
+
+    ref_out, ref_dx = O.token_grad_direct(xb, topk, gates, doutb, toks, weights_of)
+    idx_r = torch.as_tensor([r for r, _ in toks], device=DEV)
+    idx_s = torch.as_tensor([s for _, s in toks], device=DEV)
+    eo = max_row_rel(f64_of(out[idx_r, idx_s]), ref_out)
+    ed = max_row_rel(f64_of(dx[idx_r, idx_s]), ref_dx)
+    say(f"  sampled tokens: out max row rel {eo:.3e}, dx max row rel {ed:.3e}")
+    assert eo <= TOL and ed <= TOL
 
 
 def test_layer_stack_with_shared_pool():
-    """Three layers sharing one prefetch pool give bit-identical outputs and gradients to three
-    layers with their own slots (each pooled layer prefetches again before its backward), and
-    the pooled stack allocates two pools' worth less memory."""
+    """Three layers sharing one prefetch pool [AT, TL;DR; TD, memory contract]: the output, the
+    input gradient and every layer's weight gradients match the plan-free definition chained
+    through the three layers; they are bit-identical to three layers with their own slots (each
+    pooled layer prefetches again before its backward); and the pooled stack allocates two pools'
+    worth less memory."""
     cfg = MID.with_(B=2)
     layers_n = 3
     topk, gates, _ = W.routing_for(cfg)
@@ -413,6 +421,28 @@ def test_layer_stack_with_shared_pool():
     for a, b in zip(ref, got):
         assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a.view(torch.int16),
                            b.view(torch.int32) if b.dtype == torch.float32 else b.view(torch.int16))
+    # the pooled stack against the plan-free definition chained layer by layer (each layer's
+    # output and input gradient rounded to bf16, the type the layers hand on)
+    wbits = [(W.bf16_bits(a), W.bf16_bits(b)) for a, b in
+             (W.expert_weights_np(cfg.E, cfg.H, cfg.I, cfg.seed + 10 + l) for l in range(layers_n))]
+    hs = [W.hidden_rows(cfg.R, cfg.S, cfg.H, cfg.seed, "bf16")]
+    for (a, b) in wbits:
+        hs.append(W.bf16_bits(O.moe_direct(hs[-1], topk, gates, a, b).astype(np.float32)))
+    dh = W.grad_rows(cfg.R, cfg.S, cfg.H, cfg.seed, "bf16")
+    grads = [None] * layers_n
+    for l in reversed(range(layers_n)):
+        dxl, g13, g2 = O.moe_direct_backward(hs[l], topk, gates, wbits[l][0], wbits[l][1], dh)
+        grads[l] = (g13, g2)
+        dh = W.bf16_bits(dxl.astype(np.float32))
+    e_out = rel_fro(f64_of(got[0]), W.bf16_to_f32(hs[-1]).astype(np.float64))
+    e_dx = rel_fro(f64_of(got[1]), W.bf16_to_f32(dh).astype(np.float64))
+    say(f"  pooled stack vs chained oracle: out {e_out:.3e}, dx {e_dx:.3e}")
+    assert e_out <= TOL and e_dx <= TOL
+    for l in range(layers_n):
+        e13 = rel_fro(f64_of(got[2 + 2 * l]), grads[l][0])
+        e2 = rel_fro(f64_of(got[3 + 2 * l]), grads[l][1])
+        say(f"  layer {l}: dW13 {e13:.3e} dW2 {e2:.3e}")
+        assert e13 <= TOL and e2 <= TOL
     saved = used_own - used_pool
     expect = (layers_n - 1) * MoonEPPool.nbytes(cfg.R, cfg.B, cfg.H, cfg.I, training=True)["total"]
     say(f"  pooled stack saves {saved / 2**20:.1f} MiB (expected {expect / 2**20:.1f} MiB)")

@@ -205,6 +205,10 @@ def test_dispatch_full_size(maxvio):
     ("skew", {"S": 128, "H": 512, "maxvio": 4.0}),      # K = 8: scales loaded before the row
     ("balanced", {"S": 64, "H": 264, "K": 3}),          # K read at run time, ragged last batch
     ("tiny", {}),                                       # float32 rows
+    # K = 8 and rows that are whole batches of 128 vectors: the unchecked full-row form that the
+    # benchmark's combine backward runs at H = 7168 (one batch at H = 1024, two at 2048)
+    ("skew", {"S": 96, "H": 1024, "maxvio": 4.0}),
+    ("skew", {"S": 64, "H": 2048, "maxvio": 8.0}),
 ])
 def test_dispatch_row_scale(name, over):
     cfg = W.CONFIGS[name].with_(**over)
@@ -223,6 +227,33 @@ def test_dispatch_row_scale(name, over):
     assert np.all(np.abs(got - ref) <= np.abs(ref) * tol + 1e-30)
 
 
+def test_dispatch_row_scale_full_size_sampled():
+    """The combine backward exactly as the benchmark runs it (H = 7168, K = 8, full-row form):
+    every row of 64 sampled tokens against the oracle's scaled dispatch of those tokens."""
+    cfg = W.CONFIGS["skew"].with_(maxvio=4.0)
+    topk, gates, _ = W.routing_for(cfg)
+    d = dims_of(cfg)
+    say("dispatch row scale full size (sampled)")
+    _, cu, dd, st = run_plan(d, topk)
+    plan = O.make_plan(topk, cfg.E, cfg.B)
+    dest = O.destinations(topk, plan)
+    np.testing.assert_array_equal(dd.cpu().numpy(), dest)
+    dout = W.grad_rows(cfg.R, cfg.S, cfg.H, cfg.seed, "bf16")
+    dy = torch.empty((cfg.R * cfg.C, cfg.H), dtype=torch.bfloat16, device=DEV)
+    M.moonep_dispatch(d, dd, bf16_from_bits(dout), f32(gates), dy)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(9)
+    toks = [(int(r), int(s)) for r, s in zip(rng.integers(0, cfg.R, 64), rng.integers(0, cfg.S, 64))]
+    # the sampled tokens as a one-rank problem whose rows land in arrival order
+    sub_dest = np.arange(len(toks) * cfg.K).reshape(1, len(toks), cfg.K)
+    sub_x = np.stack([dout[r, s] for r, s in toks])[None]
+    sub_g = np.stack([gates[r, s] for r, s in toks])[None]
+    ref = O.dispatch(sub_dest, sub_x, row_scale=sub_g)
+    rows = torch.as_tensor(np.array([dest[r, s, k] for r, s in toks for k in range(cfg.K)]), device=DEV)
+    got = f64_of(dy[rows])
+    assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-30)
+
+
 # ----------------------------------------------------------------------------
 # combine
 # ----------------------------------------------------------------------------
@@ -231,6 +262,10 @@ def test_dispatch_row_scale(name, over):
     ("tiny", {}, True), ("tiny", {"S": 100, "lam": 2.0}, False),
     ("skew", {"S": 192, "H": 1032, "maxvio": 8.0}, True), ("balanced", {"S": 128, "H": 512, "K": 3}, True),
     ("balanced", {"S": 64, "H": 256, "K": 5}, False),
+    # rows of several 7 KiB chunks (K = 8): both forms the benchmark runs at H = 7168 (unit
+    # weights, bounds-checked; gated, full-row) and a partial last chunk at H = 4096
+    ("skew", {"S": 64, "H": 4096, "maxvio": 4.0}, False), ("skew", {"S": 64, "H": 7168, "maxvio": 4.0}, False),
+    ("skew", {"S": 64, "H": 7168, "maxvio": 4.0}, True),
 ])
 def test_combine_vs_oracle(name, over, gated):
     cfg = W.CONFIGS[name].with_(**over)

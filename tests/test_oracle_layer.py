@@ -169,3 +169,24 @@ def test_bf16_bits_round_to_nearest_even():
     b = W.bf16_bits(v)
     assert b.tolist() == [0x3F80, 0x3F80, 0x3F82, 0xC020, 0x7F62]
     assert W.bf16_to_f32(b)[0] == 1.0
+
+
+def test_expert_and_token_helpers_vs_torch_autograd():
+    """The per-expert weight gradient and the per-token output / input gradient (used where the
+    whole layer is too large for the oracle) against torch's CPU autograd in float64."""
+    cfg = W.CONFIGS["tiny"].with_(S=16, H=32, I=24)
+    topk, gates, _ = W.routing_for(cfg)
+    x = W.hidden_rows(cfg.R, cfg.S, cfg.H, 2, "f32")
+    w13, w2 = W.expert_weights_np(cfg.E, cfg.H, cfg.I, 2, std=0.2)
+    dout = W.grad_rows(cfg.R, cfg.S, cfg.H, 2, "f32")
+    xt, W13, W2, out = _torch_moe(x, topk, gates, w13, w2)
+    (out * torch.tensor(dout, dtype=torch.float64)).sum().backward()
+    for e in (0, 3, cfg.E - 1):
+        g13, g2, _ = O.expert_grad_direct(x, topk, gates, dout, e, w13[e], w2[e])
+        np.testing.assert_allclose(g13, W13.grad.numpy()[e], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(g2, W2.grad.numpy()[e], rtol=1e-10, atol=1e-12)
+    toks = [(0, 0), (1, 5), (3, 15), (2, 7)]
+    o, dx = O.token_grad_direct(x, topk, gates, dout, toks, lambda e: (w13[e], w2[e]))
+    for i, (r, s) in enumerate(toks):
+        np.testing.assert_allclose(o[i], out.detach().numpy()[r, s], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(dx[i], xt.grad.numpy()[r, s], rtol=1e-10, atol=1e-12)
