@@ -20,7 +20,8 @@ __all__ = [
     "MoonEPError", "Dims", "LIB_PATH", "lib", "NSTATS", "STAT_NAMES", "TRAINING", "F32_ROWS", "GRAD_ACCUM",
     "PHASE_GATE_UP", "PHASE_DOWN", "PHASE_DACT", "PHASE_DX", "PHASE_DW2", "PHASE_DW13",
     "ST_BAD_ID", "ST_DUP_ID", "ST_CAPACITY", "ST_OVERFLOW", "ST_TRAIN_FALLBACK",
-    "moonep_plan_workspace_bytes", "moonep_plan", "moonep_prefetch", "moonep_dispatch",
+    "moonep_plan_workspace_bytes", "moonep_plan", "moonep_plan_noalloc", "NOALLOC_WS_BYTES",
+    "moonep_prefetch", "moonep_dispatch",
     "moonep_combine", "moonep_dispatch_staged", "moonep_combine_staged", "moonep_grouped_ffn",
     "moonep_grouped_ffn_backward", "moonep_reduce_grad", "moonep_strerror", "moonep_version", "EXPORTED",
 ]
@@ -41,8 +42,9 @@ STAT_NAMES = (
     "min_rank_load", "donors", "receivers", "max_replicas_per_rank", "total_rows",
     "reserved14", "reserved15",
 )
+NOALLOC_WS_BYTES = 8 << 20     # static plan workspace of moonep_plan_noalloc, per GPU
 EXPORTED = (
-    "moonep_plan_workspace_bytes", "moonep_plan", "moonep_prefetch", "moonep_dispatch",
+    "moonep_plan_workspace_bytes", "moonep_plan", "moonep_plan_noalloc", "moonep_prefetch", "moonep_dispatch",
     "moonep_combine", "moonep_dispatch_staged", "moonep_combine_staged", "moonep_grouped_ffn",
     "moonep_grouped_ffn_backward", "moonep_reduce_grad", "moonep_strerror", "moonep_version",
 )
@@ -83,6 +85,7 @@ def _load():
     L.moonep_plan_workspace_bytes.argtypes = [P]
     L.moonep_plan_workspace_bytes.restype = SZ
     L.moonep_plan.argtypes = [P, VP, VP, VP, VP, VP, VP]
+    L.moonep_plan_noalloc.argtypes = [P, VP, VP, VP, VP, VP]
     L.moonep_prefetch.argtypes = [P, VP, VP, VP, VP, VP, VP]
     L.moonep_dispatch.argtypes = [P, VP, VP, VP, VP, VP]
     L.moonep_combine.argtypes = [P, VP, VP, VP, VP, VP]
@@ -91,7 +94,7 @@ def _load():
     L.moonep_grouped_ffn.argtypes = [P, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP]
     L.moonep_grouped_ffn_backward.argtypes = [P] + [VP] * 16
     L.moonep_reduce_grad.argtypes = [P, VP, VP, VP, VP, VP, VP]
-    for n in ("moonep_plan", "moonep_prefetch", "moonep_dispatch", "moonep_combine",
+    for n in ("moonep_plan", "moonep_plan_noalloc", "moonep_prefetch", "moonep_dispatch", "moonep_combine",
               "moonep_dispatch_staged", "moonep_combine_staged", "moonep_grouped_ffn",
               "moonep_grouped_ffn_backward", "moonep_reduce_grad"):
         getattr(L, n).restype = I32
@@ -203,6 +206,19 @@ def moonep_plan(d: Dims, topk, plan_ws, cu_seqlens, dest, stats, stream=None) ->
         _ptr(stats, "stats", torch.int32, (NSTATS,)),
     )
     _check(_lib().moonep_plan(ctypes.byref(d), *args, _stream(stream)), "moonep_plan")
+
+
+def moonep_plan_noalloc(d: Dims, topk, cu_seqlens, dest, stats, stream=None) -> None:
+    """moonep_plan with the library's static plan workspace (no device allocation); for the
+    plan + dispatch + combine path.  Calls overlapping on one GPU race."""
+    torch = _torch()
+    args = (
+        _ptr(topk, "topk", torch.int32, (d.R, d.S, d.K)),
+        _ptr(cu_seqlens, "cu_seqlens", torch.int32, (d.R, d.E + d.B + 1)),
+        _ptr(dest, "dest", torch.int32, (d.R, d.S, d.K)),
+        _ptr(stats, "stats", torch.int32, (NSTATS,)),
+    )
+    _check(_lib().moonep_plan_noalloc(ctypes.byref(d), *args, _stream(stream)), "moonep_plan_noalloc")
 
 
 def moonep_prefetch(d: Dims, plan_ws, w13_home, w2_home, w13_slot, w2_slot, stream=None) -> None:

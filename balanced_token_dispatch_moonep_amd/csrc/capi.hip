@@ -8,6 +8,7 @@ extern "C" const char* moonep_strerror(int code) {
         case MOONEP_EALIGN: return "pointer not 16-byte aligned";
         case MOONEP_EHIP: return "HIP launch failed";
         case MOONEP_ENOTSUP: return "unsupported combination of dims/flags";
+        case MOONEP_ETOOBIG: return "plan workspace larger than the static workspace of moonep_plan_noalloc";
         default: return "unknown error";
     }
 }

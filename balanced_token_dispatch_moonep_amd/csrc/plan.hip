@@ -30,6 +30,7 @@
 // Ties always go to the lower rank / expert id; integer arithmetic only, so the
 // result is bit-identical from run to run.
 #include <climits>
+#include <mutex>
 
 #include "common.h"
 
@@ -470,15 +471,11 @@ extern "C" size_t moonep_plan_workspace_bytes(const moonep_dims_t* dims) {
     return plan_ws_layout(dims, nullptr, nullptr);
 }
 
-extern "C" int moonep_plan(const moonep_dims_t* dims, const int32_t* topk, void* plan_ws,
-                           int32_t* cu_seqlens, int32_t* dest, int32_t* stats, void* stream) {
-    const int rc = check_dims(dims, false);
-    if (rc != MOONEP_OK) return rc;
-    MOONEP_CHECK_PTR(topk);
-    MOONEP_CHECK_PTR(plan_ws);
-    MOONEP_CHECK_PTR(cu_seqlens);
-    MOONEP_CHECK_PTR(dest);
-    MOONEP_CHECK_PTR(stats);
+namespace moonep {
+
+// The four planning launches on a workspace laid out by plan_ws_layout (arguments checked).
+static int launch_plan(const moonep_dims_t* dims, const int32_t* topk, void* plan_ws, int32_t* cu_seqlens,
+                       int32_t* dest, int32_t* stats, void* stream) {
     PlanWs w;
     plan_ws_layout(dims, plan_ws, &w);
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -491,4 +488,54 @@ extern "C" int moonep_plan(const moonep_dims_t* dims, const int32_t* topk, void*
     hipLaunchKernelGGL(plan_dest, dim3(w.NCH), dim3(64), 0, s, topk, w, dest);
     MOONEP_LAUNCH_CHECK();
     return MOONEP_OK;
+}
+
+// Plan workspace of moonep_plan_noalloc: one static array per GPU, held until the process ends.
+// In host code `scratch` only stands in for the symbol; its device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[MOONEP_NOALLOC_WS_BYTES];
+constexpr int kMaxDevices = 64;
+
+static int scratch_of_current_device(void** out) {
+    static std::mutex mu;
+    static void* ptrs[kMaxDevices] = {};
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOONEP_EHIP;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptrs[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOONEP_EHIP;
+        ptrs[dev] = p;
+    }
+    *out = ptrs[dev];
+    return MOONEP_OK;
+}
+
+}  // namespace moonep
+
+extern "C" int moonep_plan(const moonep_dims_t* dims, const int32_t* topk, void* plan_ws,
+                           int32_t* cu_seqlens, int32_t* dest, int32_t* stats, void* stream) {
+    const int rc = check_dims(dims, false);
+    if (rc != MOONEP_OK) return rc;
+    MOONEP_CHECK_PTR(topk);
+    MOONEP_CHECK_PTR(plan_ws);
+    MOONEP_CHECK_PTR(cu_seqlens);
+    MOONEP_CHECK_PTR(dest);
+    MOONEP_CHECK_PTR(stats);
+    return launch_plan(dims, topk, plan_ws, cu_seqlens, dest, stats, stream);
+}
+
+extern "C" int moonep_plan_noalloc(const moonep_dims_t* dims, const int32_t* topk, int32_t* cu_seqlens,
+                                   int32_t* dest, int32_t* stats, void* stream) {
+    int rc = check_dims(dims, false);
+    if (rc != MOONEP_OK) return rc;
+    MOONEP_CHECK_PTR(topk);
+    MOONEP_CHECK_PTR(cu_seqlens);
+    MOONEP_CHECK_PTR(dest);
+    MOONEP_CHECK_PTR(stats);
+    if (plan_ws_layout(dims, nullptr, nullptr) > (size_t)MOONEP_NOALLOC_WS_BYTES) return MOONEP_ETOOBIG;
+    void* ws = nullptr;
+    rc = scratch_of_current_device(&ws);
+    if (rc != MOONEP_OK) return rc;
+    return launch_plan(dims, topk, ws, cu_seqlens, dest, stats, stream);
 }

@@ -80,7 +80,8 @@ enum {
     MOONEP_EINVAL = -1,   /* bad dims or NULL pointer       */
     MOONEP_EALIGN = -2,   /* pointer not 16-byte aligned    */
     MOONEP_EHIP = -3,     /* a HIP launch failed            */
-    MOONEP_ENOTSUP = -4   /* combination not supported      */
+    MOONEP_ENOTSUP = -4,  /* combination not supported      */
+    MOONEP_ETOOBIG = -5   /* dims need a larger plan workspace than moonep_plan_noalloc holds */
 };
 
 /* Device-detected routing problems, OR-ed into stats[0]. */
@@ -124,6 +125,22 @@ size_t moonep_plan_workspace_bytes(const moonep_dims_t* dims);
  * read the home row, "fallback" [TD, memory contract]); results are bit-identical run to run. */
 int moonep_plan(const moonep_dims_t* dims, const int32_t* topk, void* plan_ws,
                 int32_t* cu_seqlens, int32_t* dest, int32_t* stats, void* stream);
+
+/* moonep_plan for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same rule and the same cu_seqlens, dest
+ * and stats, bit for bit, as moonep_plan; the plan workspace is a static device array of the
+ * library, MOONEP_NOALLOC_WS_BYTES on every GPU the library runs on, held until the process
+ * ends.  It calls no allocator.  Its output serves the plan + dispatch + combine path (dest,
+ * cu_seqlens); prefetch, grouped_ffn and reduce_grad read a caller-owned moonep_plan workspace.
+ *   topk, cu_seqlens, dest, stats  as for moonep_plan
+ * Returns MOONEP_ETOOBIG (nothing enqueued) when moonep_plan_workspace_bytes(dims) exceeds
+ * MOONEP_NOALLOC_WS_BYTES (8 MiB: e.g. R=8, E=256, S=4096, K=8 needs 2.0 MB; R=8, E=384,
+ * S=8192, K=8 about 5 MB), MOONEP_EHIP if the array's device address cannot be obtained.
+ * Every call on one GPU uses that GPU's one array: calls that overlap on a GPU (other streams,
+ * other host threads) race and must be serialised by the caller. */
+#define MOONEP_NOALLOC_WS_BYTES (8u << 20)
+int moonep_plan_noalloc(const moonep_dims_t* dims, const int32_t* topk, int32_t* cu_seqlens,
+                        int32_t* dest, int32_t* stats, void* stream);
 
 /* Weight prefetch [TC, flowchart "Weight prefetch"; TD, memory contract]: for every replica
  * that got slot j on rank q, copy the home expert's weights into that slot.
