@@ -919,7 +919,8 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_dw_kernel(GemmArgs a) {
         ipar = par;
         iseg = 0;
         ikoff = 0;
-        icur = s_seg[par][0];
+        while (iseg < nseg && s_seg[par][iseg].rows <= 0) ++iseg;   // (never for a valid plan)
+        icur = iseg < nseg ? s_seg[par][iseg] : Segment{0, 0};
     };
     auto issue = [&](int, int buf, int i) {
         const uint32_t l = lds_wave + buf * STAGE_BYTES + i * 1024;
@@ -938,8 +939,11 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_dw_kernel(GemmArgs a) {
         if (i == L::PARTS - 1) {    // step issued: advance the cursor
             ikoff += BK;
             if (__builtin_expect(ikoff >= icur.rows, 0)) {
+                // next segment with rows: an empty one (a descriptor a valid plan never makes)
+                // holds no step of nst, so the cursor must not spend one on it
                 ikoff = 0;
                 ++iseg;
+                while (iseg < nseg && s_seg[ipar][iseg].rows <= 0) ++iseg;
                 if (iseg < nseg) icur = s_seg[ipar][iseg];
             }
         }
