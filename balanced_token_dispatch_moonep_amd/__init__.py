@@ -18,6 +18,7 @@ from typing import Optional
 
 __all__ = [
     "MoonEPError", "Dims", "LIB_PATH", "lib", "NSTATS", "STAT_NAMES", "TRAINING", "F32_ROWS", "GRAD_ACCUM",
+    "PLAN_LOWMIG",
     "PHASE_GATE_UP", "PHASE_DOWN", "PHASE_DACT", "PHASE_DX", "PHASE_DW2", "PHASE_DW13",
     "ST_BAD_ID", "ST_DUP_ID", "ST_CAPACITY", "ST_OVERFLOW", "ST_TRAIN_FALLBACK",
     "moonep_plan_workspace_bytes", "moonep_plan", "moonep_plan_noalloc", "NOALLOC_WS_BYTES",
@@ -31,6 +32,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoonep.s
 TRAINING = 1
 F32_ROWS = 2
 GRAD_ACCUM = 4
+PLAN_LOWMIG = 512      # the planner's low-migration rule
 # phase selection of the expert FFN calls (one GEMM kernel each; none set = all of the call's)
 PHASE_GATE_UP, PHASE_DOWN = 8, 16
 PHASE_DACT, PHASE_DX, PHASE_DW2, PHASE_DW13 = 32, 64, 128, 256
@@ -63,9 +65,12 @@ class Dims(ctypes.Structure):
                 ("I", ctypes.c_int32), ("flags", ctypes.c_uint32)]
 
     @classmethod
-    def make(cls, R, E, B, S, K, H, I=0, training=False, f32_rows=False, grad_accum=False, phases=0) -> "Dims":
+    def make(cls, R, E, B, S, K, H, I=0, training=False, f32_rows=False, grad_accum=False, phases=0,
+             plan_rule="chain") -> "Dims":
+        if plan_rule not in ("chain", "lowmig"):
+            raise ValueError(f"unknown plan rule {plan_rule!r}")
         flags = (TRAINING if training else 0) | (F32_ROWS if f32_rows else 0) | (GRAD_ACCUM if grad_accum else 0)
-        flags |= int(phases)
+        flags |= int(phases) | (PLAN_LOWMIG if plan_rule == "lowmig" else 0)
         return cls(R, E, B, S, K, H, I, flags)
 
     def with_flags(self, flags: int) -> "Dims":

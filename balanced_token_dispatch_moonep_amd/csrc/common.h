@@ -67,7 +67,8 @@ struct PlanWs {
     Segment* fb_seg;       // [E][kMaxR]
     Segment* home_seg;     // [E]
     int32_t* counters;     // [64] tile counters of dynamically scheduled kernels
-    int32_t* dw_order;     // [E + R*B] dW targets by rows, descending (ties: lower id)
+    int32_t* dw_order;     // [E + R*B] dW targets by rows, descending (ties: lower id); written
+                           // before each weight-gradient launch
     uint16_t* zeros;       // [kZeroElems] zero bf16 row segment (source of masked GEMM tile loads)
     int32_t* tile_pref;    // [2E + 1] prefix over the groups of their 256-row GEMM tiles
 };
@@ -126,7 +127,8 @@ inline int check_dims(const moonep_dims_t* d, bool need_ffn) {
     if (d->S < 1 || d->K < 1 || d->K > kMaxK || d->K > d->E) return MOONEP_EINVAL;
     if ((int64_t)d->R * d->S * d->K > (int64_t)1 << 30) return MOONEP_EINVAL;
     if (d->H < 8 || d->H % 8 != 0) return MOONEP_EINVAL;
-    if (d->flags & ~(MOONEP_TRAINING | MOONEP_F32_ROWS | MOONEP_GRAD_ACCUM | kPhaseBits)) return MOONEP_EINVAL;
+    if (d->flags & ~(MOONEP_TRAINING | MOONEP_F32_ROWS | MOONEP_GRAD_ACCUM | MOONEP_PLAN_LOWMIG | kPhaseBits))
+        return MOONEP_EINVAL;
     if (need_ffn && (d->I < 8 || d->I % 8 != 0)) return MOONEP_EINVAL;
     return MOONEP_OK;
 }

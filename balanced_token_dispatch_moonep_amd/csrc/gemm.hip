@@ -1000,6 +1000,41 @@ __global__ void reset_counters_kernel(int* c, int n) {
     if ((int)threadIdx.x < n) c[threadIdx.x] = 0;
 }
 
+// Before a weight-gradient launch: reset its tile counter and order the dW targets (home experts
+// with their fallback replicas, then slots) by rows, descending, ties to the lower index, so the
+// kernel hands out the largest first (longest-processing-time order).  The order only schedules
+// tiles: every target's result is the same in any order.
+constexpr int kOrderThreads = 512;
+__global__ __launch_bounds__(kOrderThreads) void dw_prepare_kernel(PlanWs w, int* counter) {
+    extern __shared__ unsigned long long okey[];   // [E + R*B]
+    const int tid = threadIdx.x;
+    const int ntarget = w.E + w.R * w.B;
+    if (tid == 0) *counter = 0;
+    for (int t = tid; t < ntarget; t += kOrderThreads) {
+        int rows = 0;
+        if (t < w.E) {
+            const Segment hs = w.home_seg[t];
+            rows = seg_ok(hs, w) ? hs.rows : 0;
+            const int nfb = min(max(w.fb_n[t], 0), kMaxR - 1);
+            for (int i = 0; i < nfb; ++i) {
+                const Segment f = w.fb_seg[(size_t)t * kMaxR + i];
+                rows += seg_ok(f, w) ? f.rows : 0;
+            }
+        } else if (w.slot_e[t - w.E] >= 0) {
+            rows = max(w.slot_rows[t - w.E], 0);
+        }
+        okey[t] = ((unsigned long long)(unsigned)rows << 32) | (unsigned)(~t);
+    }
+    __syncthreads();
+    for (int t = tid; t < ntarget; t += kOrderThreads) {
+        const unsigned long long k = okey[t];
+        int rank = 0;
+#pragma unroll 8
+        for (int u = 0; u < ntarget; ++u) rank += okey[u] > k;
+        w.dw_order[rank] = t;
+    }
+}
+
 static int g_num_cu = 0;
 static int num_cus() {
     if (g_num_cu <= 0) {
@@ -1050,14 +1085,18 @@ static int launch_rows(int epi, int mode, const GemmArgs& a0, hipStream_t s) {
     return MOONEP_OK;
 }
 
-// Resets the launch's tile counter, then runs the dynamic-tile weight-gradient kernel.
+// Resets the launch's tile counter and orders the targets, then runs the dynamic-tile
+// weight-gradient kernel.
 template <int WHICH>
 static int launch_dw(const GemmArgs& a, hipStream_t s) {
     constexpr int WN = MOONEP_WN_DW;
     constexpr int smem = dw_smem<WN>();
     static bool ok = set_smem(gemm_dw_kernel<WN, WHICH>, smem);
     if (!ok) return MOONEP_EHIP;
-    hipLaunchKernelGGL(reset_counters_kernel, dim3(1), dim3(64), 0, s, a.counter, 1);
+    const size_t okey_bytes = (size_t)(a.w.E + a.w.R * a.w.B) * sizeof(unsigned long long);
+    static bool ok_order = set_smem(dw_prepare_kernel, (int)((kMaxE + kMaxR * kMaxB) * sizeof(unsigned long long)));
+    if (!ok_order) return MOONEP_EHIP;
+    hipLaunchKernelGGL(dw_prepare_kernel, dim3(1), dim3(kOrderThreads), okey_bytes, s, a.w, a.counter);
     MOONEP_LAUNCH_CHECK();
     const int grid = (num_cus() / 8) * 8;
     hipLaunchKernelGGL((gemm_dw_kernel<WN, WHICH>), dim3(grid), dim3(128 * WN), smem, s, a);

@@ -31,7 +31,8 @@ SWEEP = (0.0, 0.5, 2.0, 4.0, 8.0)
 
 # timed call -> the one kernel it launches (name as in rocprofv3 kernel traces); the plan call
 # launches four small kernels and has no entry.  The weight-gradient calls also launch a
-# one-wave counter reset before their GEMM, the row GEMM calls a one-wave tile prefix.
+# one-workgroup kernel that resets their tile counter and orders their targets before the GEMM,
+# the row GEMM calls a one-wave counter reset and a one-wave tile prefix.
 KERNEL_NAMES = {
     "prefetch": "moonep::prefetch_kernel",
     "dispatch": "moonep::dispatch_kernel<false, false, 0, 2, false, true>",
@@ -278,6 +279,10 @@ def main():
         c = W.LOGNORMAL
         dl = M.Dims.make(c["R"], c["E"], B, c["S"], c["K"], H)
         Ll = MoonEPLayer(dl, training=False)
+        # the same workload under the low-migration plan rule (plan only: the rows differ, the
+        # dispatch and combine bytes do not)
+        dlo = M.Dims.make(c["R"], c["E"], B, c["S"], c["K"], H, plan_rule="lowmig")
+        Llo = MoonEPLayer(dlo, training=False)
         xl = torch.randn((c["R"], c["S"], H), device=dev).to(torch.bfloat16)
         with open(os.path.join(ROOT, "tests", "golden", "lognormal_table1.json")) as f:
             post = {row[0]: row for row in json.load(f)["rows"]}
@@ -293,9 +298,12 @@ def main():
                 if it == 0:
                     torch.cuda.synchronize()
                     T4.clear()
+            for it in range(4):
+                T4.run("plan_lowmig", lambda: Llo.plan(tkd))
             torch.cuda.synchronize()
             m4 = T4.avg_ms()
             s4 = Ll.stats.cpu().numpy()
+            s5 = Llo.stats.cpu().numpy()
             cap = c["S"] * c["K"]
             rows_l = c["R"] * cap
             dcb = 2 * (c["R"] * c["S"] * H * 2 + rows_l * H * 2) + 12.0 * rows_l
@@ -306,12 +314,14 @@ def main():
                 "migrated_pct": round(100.0 * int(s4[5]) / rows_l, 2),
                 "migration_bound_pct": round(100.0 * int(s4[6]) / rows_l, 2),
                 "copies": int(s4[1]), "fallback": int(s4[3]), "plan_us": round(m4["plan"] * 1e3, 1),
+                "lowmig": {"migrated_pct": round(100.0 * int(s5[5]) / rows_l, 2), "copies": int(s5[1]),
+                           "fallback": int(s5[3]), "plan_us": round(m4["plan_lowmig"] * 1e3, 1)},
                 "dc_GBps": round(dcb / ((m4["dispatch"] + m4["combine"]) / 1e3) / 1e9, 1),
                 "post_table1": None if p is None else {"peak_over_mean": p[3], "migrated_pct": p[5],
                                                        "copy_slots": p[6]},
             })
             log("[bench] lognormal", lognormal[-1])
-        del Ll, xl
+        del Ll, Llo, xl
 
     # ---- zero-copy ablation: the staged baseline (arrival-order copy + sort-copy) ------------
     ablation = None

@@ -62,6 +62,11 @@ typedef struct moonep_dims {
 #define MOONEP_TRAINING 1u   /* plan for training: a fallback replica sets MOONEP_ST_TRAIN_FALLBACK */
 #define MOONEP_F32_ROWS 2u   /* dispatch/combine rows are float32 instead of bf16 */
 #define MOONEP_GRAD_ACCUM 4u /* grouped_ffn_backward adds into dw*_home / dw*_red instead of writing them */
+/* moonep_plan / moonep_plan_noalloc: the low-migration rule instead of the default chain.  Both
+ * keep exactly S*K rows and at most one remote home group per rank; this one moves fewer rows
+ * under strong skew ([TC, What we measured, Table 1] "migrated tokens"), e.g. 38.1% instead of
+ * 44.2% of all rows at the lognormal sigma = 5 workload, where the exact minimum is 38.1%. */
+#define MOONEP_PLAN_LOWMIG 512u
 
 /* Phase selection for the expert FFN calls.  Each phase is one GEMM kernel.  A call runs the
  * phases of its own that are set in flags, in the order listed; with none of its phases set it

@@ -17,12 +17,13 @@ the MoonEP pages it follows; where the pages leave a step open the reading
 taken is stated at the function.
 """
 from .plan import (RoutingError, CapacityError, Plan, validate_routing, expert_counts,
-                   maxvio, make_plan, destinations, stats_vector, STAT_NAMES,
+                   maxvio, make_plan, destinations, stats_vector, STAT_NAMES, RULES,
                    ST_BAD_ID, ST_DUP_ID, ST_CAPACITY, ST_OVERFLOW, ST_TRAIN_FALLBACK)
 from .layer import (dispatch, combine, groups, prefetch, ffn_forward, ffn_backward,
                     reduce_grad, moe_direct, moe_direct_backward, silu, swiglu_ffn,
                     swiglu_ffn_backward, expert_grad_direct, token_grad_direct)
-from .brute import min_replicas_milp, min_replicas_enum, plan_is_feasible_flow
+from .brute import (min_replicas_milp, min_replicas_enum, plan_is_feasible_flow, min_migration_milp,
+                    min_migration_enum)
 from .memory import buffer_bytes
 
 __all__ = [
@@ -32,5 +33,5 @@ __all__ = [
     "prefetch", "ffn_forward", "ffn_backward", "reduce_grad", "moe_direct",
     "moe_direct_backward", "silu", "swiglu_ffn", "swiglu_ffn_backward", "expert_grad_direct",
     "token_grad_direct", "min_replicas_milp", "min_replicas_enum",
-    "plan_is_feasible_flow", "buffer_bytes",
+    "plan_is_feasible_flow", "min_migration_milp", "min_migration_enum", "buffer_bytes", "RULES",
 ]

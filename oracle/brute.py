@@ -1,4 +1,4 @@
-"""Oracle: exact minimum number of redundant experts, to pin the plan rule.
+"""Oracle: exact minimum number of redundant experts and of migrated rows, to pin the plan rules.
 
 TEST INFRASTRUCTURE ONLY.  Page abbreviations as in ``oracle.plan``.
 
@@ -16,6 +16,16 @@ integration].  Two independent exact solvers give the least number of
   more of its own).  The set is feasible iff the flow saturates sum max(0, X).
 * ``min_replicas_milp``: the same problem as a mixed-integer program (HiGHS via
   scipy), usable at sizes where enumeration is too slow.
+
+The fewest rows that must leave their home rank ("migrated tokens" [TC, What we measured,
+Table 1]) under the same one-remote-group property, two ways:
+
+* ``min_migration_enum``: every map of ranks to the one remote home group they may serve (or
+  none) is enumerated (tiny inputs); for each, the least rows moved is a linear program (a
+  transshipment over the arcs the map allows, whose optimum is integral), solved with HiGHS.
+* ``min_migration_milp``: one mixed-integer program over the arcs and the host choice.
+Without the property the least is sum over ranks of max(0, X), every donor shipping its excess
+straight to receivers (``one_group=False``).
 """
 from __future__ import annotations
 
@@ -23,7 +33,7 @@ import itertools
 from typing import Iterable, Optional, Sequence, Tuple
 
 import numpy as np
-from scipy.optimize import Bounds, LinearConstraint, milp
+from scipy.optimize import Bounds, LinearConstraint, linprog, milp
 from scipy.sparse import csr_matrix
 from scipy.sparse.csgraph import maximum_flow
 
@@ -150,6 +160,96 @@ def min_replicas_milp(L: Sequence[int], R: int, E: int, C: int, one_group: bool 
         hidx = {h: 2 * na + k for k, h in enumerate(hosts)}
         for i, (e, q) in enumerate(arcs):
             row([(i, 1.0), (hidx[(q, e // G)], -1.0)], -np.inf, 0.0)
+        for q in range(R):
+            row([(hidx[(q, d)], 1.0) for d in range(R) if d != q], -np.inf, 1.0)
+    res = milp(cobj, integrality=integrality, bounds=Bounds(np.zeros(nv), ub),
+               constraints=LinearConstraint(np.array(rows), np.array(lo), np.array(hi)))
+    if not res.success:
+        raise RuntimeError("MILP failed: " + str(res.message))
+    return int(round(res.fun))
+
+
+def _migration_rows(L, R, E, C, allowed, one_group):
+    """Constraint rows of the least-migration problem over arcs (e, q), h(e) != q, allowed(e, q)."""
+    G = E // R
+    X = _excess(L, R, E, C)
+    arcs = [(e, q) for e in range(E) for q in range(R) if e // G != q and L[e] > 0 and allowed(e, q)]
+    return G, X, arcs
+
+
+def min_migration_enum(L: Sequence[int], R: int, E: int, C: int) -> int:
+    """Least migrated rows with at most one remote home group per rank, by enumerating every
+    host map and solving the transshipment LP each allows (tiny inputs only: R**R maps)."""
+    L = np.asarray(L, dtype=np.int64)
+    best = None
+    for hosts in itertools.product(range(-1, R), repeat=R):
+        if any(h == q for q, h in enumerate(hosts)):
+            continue
+        G, X, arcs = _migration_rows(L, R, E, C, lambda e, q: hosts[q] == e // (E // R), True)
+        if not np.any(X):
+            return 0
+        if not arcs:
+            continue
+        na = len(arcs)
+        a_eq = np.zeros((R, na))
+        for i, (e, q) in enumerate(arcs):
+            a_eq[e // G, i] -= 1.0          # rows leave the home rank of e
+            a_eq[q, i] += 1.0               # and arrive at q
+        a_ub = np.zeros((E, na))
+        for i, (e, q) in enumerate(arcs):
+            a_ub[e, i] = 1.0                # an expert cannot give more rows than it has
+        res = linprog(np.ones(na), A_ub=a_ub, b_ub=L.astype(float), A_eq=a_eq, b_eq=(-X).astype(float),
+                      bounds=[(0, None)] * na, method="highs")
+        if res.status == 0:
+            v = int(round(res.fun))
+            best = v if best is None else min(best, v)
+    if best is None:
+        raise RuntimeError("no feasible host map")
+    return best
+
+
+def min_migration_milp(L: Sequence[int], R: int, E: int, C: int, one_group: bool = True) -> int:
+    """Least migrated rows as a MILP.
+
+    Variables: f[e,q] >= 0 rows of e served on rank q != h(e); y[q,d] in {0,1} (rank q serves
+    home group d) when ``one_group``.  Constraints: sum_q f[e,q] <= L[e]; for every rank q,
+    (rows of others' experts served on q) - (rows of q's experts served elsewhere) = -X[q];
+    f[e,q] <= L[e] y[q,h(e)]; sum_d y[q,d] <= 1.  Objective: minimise sum f."""
+    L = np.asarray(L, dtype=np.int64)
+    G, X, arcs = _migration_rows(L, R, E, C, lambda e, q: True, one_group)
+    if not np.any(X):
+        return 0
+    na = len(arcs)
+    hosts = [(q, d) for q in range(R) for d in range(R) if d != q] if one_group else []
+    nh = len(hosts)
+    hidx = {h: na + k for k, h in enumerate(hosts)}
+    nv = na + nh
+    cobj = np.zeros(nv)
+    cobj[:na] = 1.0
+    integrality = np.zeros(nv)
+    integrality[na:] = 1
+    ub = np.concatenate([np.array([L[e] for (e, q) in arcs], float), np.ones(nh)])
+    rows, lo, hi = [], [], []
+
+    def row(coefs, l, h):
+        v = np.zeros(nv)
+        for i, c in coefs:
+            v[i] += c
+        rows.append(v)
+        lo.append(l)
+        hi.append(h)
+
+    for e in range(E):
+        co = [(i, 1.0) for i, (ee, q) in enumerate(arcs) if ee == e]
+        if co:
+            row(co, -np.inf, float(L[e]))
+    for q in range(R):
+        co = [(i, -1.0) for i, (e, t) in enumerate(arcs) if e // G == q]
+        co += [(i, 1.0) for i, (e, t) in enumerate(arcs) if t == q]
+        row(co, float(-X[q]), float(-X[q]))
+    if one_group:
+        for i, (e, q) in enumerate(arcs):
+            row([(i, 1.0), (hidx[(q, e // G)], -float(L[e]))], -np.inf, 0.0)
         for q in range(R):
             row([(hidx[(q, d)], 1.0) for d in range(R) if d != q], -np.inf, 1.0)
     res = milp(cobj, integrality=integrality, bounds=Bounds(np.zeros(nv), ub),

@@ -135,7 +135,10 @@ class Plan:
         return self.S * self.K
 
 
-def make_plan(topk: np.ndarray, E: int, B: int, training: bool = False) -> Plan:
+RULES = ("chain", "lowmig")
+
+
+def make_plan(topk: np.ndarray, E: int, B: int, training: bool = False, rule: str = "chain") -> Plan:
     """Plan redundant experts so every rank serves exactly C = S*K rows.
 
     Steps (notation: G = E/R home experts per rank, h(e) = e // G its home rank):
@@ -164,6 +167,22 @@ def make_plan(topk: np.ndarray, E: int, B: int, training: bool = False) -> Plan:
        Table 1].
     7. Instances.  Expert e is served first by its home rank (keep[e] rows), then by
        its replicas in creation order; the instance start offsets partition e's rows.
+
+    ``rule="lowmig"`` replaces step 4 by a chain that moves fewer rows (fewer "migrated
+    tokens" [TC, What we measured, Table 1]) under the same one-remote-group property:
+
+    4'. Walk the donors in order; rem = the rows the donor must still ship.  A donor first
+        repays a shortfall inherited from the previous donor, as in step 4.  The last donor
+        then covers every receiver left.  Any other donor covers, again and again, the
+        largest remaining receiver whose whole deficit fits in rem (ties to the lower
+        rank).  When none fits and rem > 0, it either (a) covers the smallest remaining
+        receiver whole (ties to the lower rank), falling s = deficit - rem rows short,
+        which the next donor repays (step 4's carry, s rows moved twice), or (b) hands its
+        rem rows to the next donor, which then ships rem more of its own (rem rows moved
+        twice).  It takes (a) only when s < rem and it was handed no rows itself: a rank
+        handed rows by the previous donor already serves that donor's group, and repaying
+        would add the next donor's group.  Every rank still gets replicas from one ship
+        call, so from at most one other home group.
     """
     topk = np.asarray(topk)
     validate_routing(topk, E)
@@ -203,28 +222,74 @@ def make_plan(topk: np.ndarray, E: int, B: int, training: bool = False) -> Plan:
             avail[e] -= a
             amt -= a
 
-    # 4. chain
-    j = 0
-    carry = None          # (previous donor, rows it is short of C)
-    for d in donors:
-        rem = int(X[d])
-        if carry is not None:
-            t, s = carry
-            ship(d, t, s)
-            rem -= s
-            carry = None
-        while rem > 0 and j < len(receivers):
-            t = receivers[j]
-            need = int(-X[t])
-            ship(d, t, need)
-            rem -= need
-            j += 1
-        if rem < 0:
-            carry = (d, -rem)
-        elif rem > 0:
-            raise CapacityError("excess left with no receiver")
-    if carry is not None or j != len(receivers):
-        raise CapacityError("chain did not close")
+    if rule == "chain":
+        # 4. chain
+        j = 0
+        carry = None          # (previous donor, rows it is short of C)
+        for d in donors:
+            rem = int(X[d])
+            if carry is not None:
+                t, s = carry
+                ship(d, t, s)
+                rem -= s
+                carry = None
+            while rem > 0 and j < len(receivers):
+                t = receivers[j]
+                need = int(-X[t])
+                ship(d, t, need)
+                rem -= need
+                j += 1
+            if rem < 0:
+                carry = (d, -rem)
+            elif rem > 0:
+                raise CapacityError("excess left with no receiver")
+        if carry is not None or j != len(receivers):
+            raise CapacityError("chain did not close")
+    elif rule == "lowmig":
+        # 4'. packing chain with carries in either direction
+        left = list(receivers)            # deficit desc, rank asc
+        carry = None                      # (previous donor, rows it is short of C)
+        handed = 0                        # rows the previous donor handed to this one
+        for i, d in enumerate(donors):
+            rem = int(X[d]) + handed
+            may_repay = handed == 0
+            handed = 0
+            if carry is not None:
+                t, s = carry
+                ship(d, t, s)
+                rem -= s
+                carry = None
+            if i == len(donors) - 1:
+                for t in left:
+                    ship(d, t, int(-X[t]))
+                    rem += int(X[t])
+                left = []
+            while rem > 0 and left:
+                fit = [t for t in left if -X[t] <= rem]
+                if fit:
+                    t = fit[0]
+                    ship(d, t, int(-X[t]))
+                    rem += int(X[t])
+                    left.remove(t)
+                    continue
+                small = min(int(-X[t]) for t in left)
+                t = next(t for t in left if -X[t] == small)
+                if may_repay and small - rem < rem:
+                    ship(d, t, small)         # (a) short by small - rem, repaid by the next donor
+                    rem -= small
+                    left.remove(t)
+                else:
+                    ship(d, donors[i + 1], rem)   # (b) the next donor ships these rows on
+                    handed = rem
+                    rem = 0
+            if rem < 0:
+                carry = (d, -rem)
+            elif rem > 0:
+                raise CapacityError("excess left with no receiver")
+        if carry is not None or handed or left:
+            raise CapacityError("chain did not close")
+    else:
+        raise ValueError(f"unknown plan rule {rule!r}")
 
     # 5. slots / fallback
     per_rank = [0] * R

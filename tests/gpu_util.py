@@ -23,10 +23,10 @@ def say(*a):
     sys.stdout.flush()
 
 
-def dims_of(cfg: W.Config, B=None, training=False, f32_rows=None) -> M.Dims:
+def dims_of(cfg: W.Config, B=None, training=False, f32_rows=None, rule="chain") -> M.Dims:
     f32 = (cfg.dtype == "f32") if f32_rows is None else f32_rows
     return M.Dims.make(cfg.R, cfg.E, cfg.B if B is None else B, cfg.S, cfg.K, cfg.H, cfg.I,
-                       training=training, f32_rows=f32)
+                       training=training, f32_rows=f32, plan_rule=rule)
 
 
 def i32(a) -> torch.Tensor:
@@ -65,8 +65,10 @@ def run_plan(d: M.Dims, topk: np.ndarray, topk_dev=None):
 
 
 def assert_plan_parity(d: M.Dims, topk: np.ndarray, training=False):
-    """Bit-exact cu_seqlens, dest and stats against the oracle; returns (oracle plan, dest, GPU tuple)."""
-    plan = O.make_plan(topk, d.E, d.B, training=training)
+    """Bit-exact cu_seqlens, dest and stats against the oracle (the plan rule the dims' flags
+    select); returns (oracle plan, dest, GPU tuple)."""
+    rule = "lowmig" if d.flags & M.PLAN_LOWMIG else "chain"
+    plan = O.make_plan(topk, d.E, d.B, training=training, rule=rule)
     dest = O.destinations(topk, plan)
     ws, cu, dd, st = run_plan(d, topk)
     np.testing.assert_array_equal(cu.cpu().numpy(), plan.cu)

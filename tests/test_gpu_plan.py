@@ -30,20 +30,24 @@ def _gold():
 def test_plan_worked_examples(case):
     say("plan worked example", case["name"])
     topk = np.array(case["topk"], dtype=np.int32)
-    d = M.Dims.make(case["R"], case["E"], case["B"], case["S"], case["K"], 8)
+    d = M.Dims.make(case["R"], case["E"], case["B"], case["S"], case["K"], 8, plan_rule=case.get("rule", "chain"))
     plan, dest, (ws, cu, dd, st) = assert_plan_parity(d, topk)
     assert dd.cpu().numpy().tolist() == case["dest"]
     assert cu.cpu().numpy().tolist() == case["cu"]
 
 
+RULES = ("chain", "lowmig")
+
+
+@pytest.mark.parametrize("rule", RULES)
 @pytest.mark.parametrize("lam", [0.0, 0.5, 1.0, 2.0])
 @pytest.mark.parametrize("B", [0, 2, 4])
-def test_plan_tiny_sweep(lam, B):
+def test_plan_tiny_sweep(lam, B, rule):
     for seed in range(5):
         cfg = W.CONFIGS["tiny"].with_(lam=lam, seed=seed)
         topk, _, _ = W.routing_for(cfg)
-        say("plan tiny", lam, B, seed)
-        assert_plan_parity(dims_of(cfg, B=B, training=True), topk, training=True)
+        say("plan tiny", lam, B, seed, rule)
+        assert_plan_parity(dims_of(cfg, B=B, training=True, rule=rule), topk, training=True)
 
 
 def _degenerate_routing(kind, R, E, S, K):
@@ -64,15 +68,16 @@ def _degenerate_routing(kind, R, E, S, K):
     return np.ascontiguousarray(t, dtype=np.int32)
 
 
+@pytest.mark.parametrize("rule", RULES)
 @pytest.mark.parametrize("kind", ["single_hot", "own_home", "round_robin", "next_rank"])
 @pytest.mark.parametrize("B,training", [(0, False), (2, False), (4, True)])
-def test_plan_degenerate_routings(kind, B, training):
+def test_plan_degenerate_routings(kind, B, training, rule):
     """Routings at the ends of the method's range, bit-exact against the oracle: all load on one
     rank (most replicas, fallback when slots run out), none to move, and every pair remote."""
     R, E, S, K = 8, 64, 96, 4
     topk = _degenerate_routing(kind, R, E, S, K)
-    say("plan degenerate", kind, B, training)
-    d = M.Dims.make(R, E, B, S, K, 8, training=training)
+    say("plan degenerate", kind, B, training, rule)
+    d = M.Dims.make(R, E, B, S, K, 8, training=training, plan_rule=rule)
     plan, dest, (ws, cu, dd, st) = assert_plan_parity(d, topk, training=training)
     if kind in ("own_home", "round_robin", "next_rank"):
         assert len(plan.entries) == 0          # every rank already serves exactly S*K rows
@@ -84,21 +89,26 @@ def test_plan_degenerate_routings(kind, B, training):
     (8, 64, 128, 4, 2, 0.5), (8, 64, 130, 4, 8, 1.5), (2, 16, 64, 8, 1, 1.0),
     (1, 8, 32, 2, 0, 1.0), (8, 256, 64, 8, 4, 0.3), (4, 8, 65, 8, 2, 0.0), (16, 512, 96, 8, 3, 0.8),
     (3, 12, 200, 3, 1, 1.2),
+    # 64 home experts per rank, the most a rank's group may hold (one lane per expert in the
+    # planner's replica chain)
+    (2, 128, 128, 8, 4, 1.0), (8, 512, 96, 8, 4, 0.8), (4, 256, 64, 8, 0, 1.5),
 ])
-def test_plan_shapes(R, E, S, K, B, lam):
+@pytest.mark.parametrize("rule", RULES)
+def test_plan_shapes(R, E, S, K, B, lam, rule):
     cfg = W.Config("m", R=R, E=E, B=B, S=S, K=K, H=8, I=0, dtype="f32", lam=lam, seed=3)
     topk, _, _ = W.routing_for(cfg)
-    say("plan shape", R, E, S, K, B, lam)
-    assert_plan_parity(dims_of(cfg), topk)
+    say("plan shape", R, E, S, K, B, lam, rule)
+    assert_plan_parity(dims_of(cfg, rule=rule), topk)
 
 
+@pytest.mark.parametrize("rule", RULES)
 @pytest.mark.parametrize("maxvio", [0.0, 0.5, 2.0, 4.0, 8.0])
-def test_plan_full_size(maxvio):
+def test_plan_full_size(maxvio, rule):
     cfg = W.CONFIGS["skew"].with_(maxvio=maxvio)
     topk, _, _ = W.routing_for(cfg)
-    say("plan full size maxvio", maxvio)
+    say("plan full size maxvio", maxvio, rule)
     for B in (4, 3):
-        plan, dest, (ws, cu, dd, st) = assert_plan_parity(dims_of(cfg, B=B), topk)
+        plan, dest, (ws, cu, dd, st) = assert_plan_parity(dims_of(cfg, B=B, rule=rule), topk)
         s = st.cpu().numpy()
         assert s[13] == cfg.R * cfg.C and s[0] == 0
 
@@ -378,13 +388,14 @@ def test_staged_full_size_matches_fused():
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
 
 
+@pytest.mark.parametrize("rule", RULES)
 @pytest.mark.parametrize("sigma", [0.0, 0.5, 1.0, 2.0, 5.0])
-def test_plan_lognormal(sigma):
+def test_plan_lognormal(sigma, rule):
     """The planner workload of the thakicloud.com post (Table 1 setup), bit-exact to the oracle."""
     c = W.LOGNORMAL
     topk, _ = W.lognormal_routing(c["R"], c["S"], c["E"], c["K"], sigma)
-    d = M.Dims.make(c["R"], c["E"], 4, c["S"], c["K"], 128)
-    say("plan lognormal sigma", sigma)
+    d = M.Dims.make(c["R"], c["E"], 4, c["S"], c["K"], 128, plan_rule=rule)
+    say("plan lognormal sigma", sigma, rule)
     plan, dest, (ws, cu, dd, st) = assert_plan_parity(d, np.array(topk))
     assert np.all(cu.cpu().numpy()[:, -1] == c["S"] * c["K"])
 

@@ -73,7 +73,7 @@ def _gold_cases():
 @pytest.mark.parametrize("case", _gold_cases(), ids=lambda c: c["name"])
 def test_worked_examples(case):
     topk = np.array(case["topk"], dtype=np.int32)
-    plan = O.make_plan(topk, case["E"], case["B"])
+    plan = O.make_plan(topk, case["E"], case["B"], rule=case.get("rule", "chain"))
     assert [[en.e, en.q, en.a] for en in plan.entries] == case["entries"]
     assert plan.cu.tolist() == case["cu"]
     dest = O.destinations(topk, plan)
@@ -141,8 +141,9 @@ def test_already_balanced_is_a_stable_sort(R, E, S, K):
     _plan_props(topk, plan, dest)
 
 
+@pytest.mark.parametrize("rule", O.RULES)
 @pytest.mark.parametrize("R,K,S", [(8, 8, 16), (8, 4, 16), (8, 2, 8), (4, 2, 32), (4, 4, 8)])
-def test_single_hot_routing(R, K, S):
+def test_single_hot_routing(R, K, S, rule):
     """Every token picks experts 0..K-1 (K <= G, K | R).
 
     L[e] = R*S = (R/K)*C for e < K, all in rank 0's group: rank 0 is the only donor with
@@ -153,7 +154,7 @@ def test_single_hot_routing(R, K, S):
     G = 8
     E = G * R
     topk = np.tile(np.arange(K, dtype=np.int32), (R, S, 1))
-    plan = O.make_plan(topk, E, B=G)
+    plan = O.make_plan(topk, E, B=G, rule=rule)
     C = S * K
     assert len(plan.entries) == R - 1
     assert [(en.e, en.q, en.a) for en in plan.entries] == [((q - 1) * K // R, q, C) for q in range(1, R)]
@@ -164,12 +165,13 @@ def test_single_hot_routing(R, K, S):
     _plan_props(topk, plan, dest)
 
 
-def test_slots_equal_group_never_fall_back():
+@pytest.mark.parametrize("rule", O.RULES)
+def test_slots_equal_group_never_fall_back(rule):
     """B = E/R covers every duplicate a rank can receive (one remote group of E/R experts)."""
     for seed in range(20):
         cfg = W.CONFIGS["tiny"].with_(seed=seed, lam=2.0)
         topk, _, _ = W.routing_for(cfg)
-        plan = O.make_plan(topk, cfg.E, cfg.G)
+        plan = O.make_plan(topk, cfg.E, cfg.G, rule=rule)
         assert all(en.w >= cfg.E for en in plan.entries)
 
 
@@ -191,13 +193,14 @@ def test_fallback_does_not_change_rows_per_rank():
 # properties over configurations and seeds
 # ----------------------------------------------------------------------------
 
+@pytest.mark.parametrize("rule", O.RULES)
 @pytest.mark.parametrize("lam", [0.0, 0.25, 0.5, 1.0, 2.0])
-def test_properties_seed_sweep_tiny(lam):
+def test_properties_seed_sweep_tiny(lam, rule):
     for seed in range(20):
         cfg = W.CONFIGS["tiny"].with_(seed=seed, lam=lam)
         topk, _, _ = W.routing_for(cfg)
         for B in (0, 2, cfg.B):
-            plan = O.make_plan(topk, cfg.E, B)
+            plan = O.make_plan(topk, cfg.E, B, rule=rule)
             _plan_props(topk, plan, O.destinations(topk, plan))
 
 
@@ -205,19 +208,21 @@ def test_properties_seed_sweep_tiny(lam):
     (8, 64, 128, 4, 2, 0.5), (8, 64, 128, 4, 8, 1.5), (2, 16, 64, 8, 1, 1.0),
     (1, 8, 32, 2, 0, 1.0), (8, 256, 64, 8, 4, 0.3), (4, 8, 64, 8, 2, 0.0),
 ])
-def test_properties_mid_shapes(R, E, S, K, B, lam):
+@pytest.mark.parametrize("rule", O.RULES)
+def test_properties_mid_shapes(R, E, S, K, B, lam, rule):
     cfg = W.Config("m", R=R, E=E, B=B, S=S, K=K, H=8, I=0, dtype="f32", lam=lam, seed=3)
     topk, _, _ = W.routing_for(cfg)
-    plan = O.make_plan(topk, E, B)
+    plan = O.make_plan(topk, E, B, rule=rule)
     _plan_props(topk, plan, O.destinations(topk, plan))
 
 
 @pytest.mark.slow
+@pytest.mark.parametrize("rule", O.RULES)
 @pytest.mark.parametrize("maxvio", [0.0, 0.5, 2.0, 4.0, 8.0])
-def test_properties_full_size(maxvio):
+def test_properties_full_size(maxvio, rule):
     cfg = W.CONFIGS["skew"].with_(maxvio=maxvio)
     topk, _, _ = W.routing_for(cfg)
-    plan = O.make_plan(topk, cfg.E, cfg.B)
+    plan = O.make_plan(topk, cfg.E, cfg.B, rule=rule)
     dest = O.destinations(topk, plan)
     _plan_props(topk, plan, dest)
     if maxvio:
@@ -257,13 +262,63 @@ def test_flow_check_on_a_plan():
 
 @pytest.mark.parametrize("lam", [0.0, 0.25, 0.5, 1.0, 2.0])
 def test_rule_reaches_minimum_replicas(lam):
-    """Tiny layer (R4 E16 S64 K2), seeds 0..99: the rule's duplicate count equals the least
+    """Tiny layer (R4 E16 S64 K2), seeds 0..99: both rules' duplicate count equals the least
     count any plan with at most one remote home group per rank can achieve."""
     for seed in range(100):
         cfg = W.CONFIGS["tiny"].with_(seed=seed, lam=lam)
         topk, _, _ = W.routing_for(cfg)
-        plan = O.make_plan(topk, cfg.E, cfg.B)
-        assert len(plan.entries) == O.min_replicas_milp(plan.L, cfg.R, cfg.E, cfg.C), (lam, seed)
+        least = None
+        for rule in O.RULES:
+            plan = O.make_plan(topk, cfg.E, cfg.B, rule=rule)
+            least = least or O.min_replicas_milp(plan.L, cfg.R, cfg.E, cfg.C)
+            assert len(plan.entries) == least, (lam, seed, rule)
+
+
+# ----------------------------------------------------------------------------
+# least number of migrated rows
+# ----------------------------------------------------------------------------
+
+def test_min_migration_milp_agrees_with_enumeration():
+    """The least-migration MILP is pinned to enumeration of every host map with one LP each on
+    very small inputs; without the one-group property it is the closed form sum max(0, X)."""
+    checked = 0
+    for (R, E, S, K) in [(3, 6, 8, 2), (4, 8, 8, 2)]:
+        for lam in (0.5, 1.0, 2.0):
+            for seed in range(3):
+                cfg = W.Config("b", R=R, E=E, B=2, S=S, K=K, H=8, I=0, dtype="f32", lam=lam, seed=seed)
+                topk, _, _ = W.routing_for(cfg)
+                _, L = O.expert_counts(topk, E)
+                G = E // R
+                X = np.array([L[q * G:(q + 1) * G].sum() for q in range(R)]) - S * K
+                assert O.min_migration_milp(L, R, E, S * K) == O.min_migration_enum(L, R, E, S * K)
+                assert O.min_migration_milp(L, R, E, S * K, one_group=False) == int(np.maximum(X, 0).sum())
+                checked += 1
+    assert checked == 18
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("workload", ["lognormal sigma 1", "lognormal sigma 5", "zipf maxvio 4",
+                                      "zipf maxvio 8"])
+def test_lowmig_reaches_least_migration(workload):
+    """Under strong skew the low-migration rule moves exactly the least number of rows any plan
+    with at most one remote home group per rank can (the exact MILP optimum), and fewer than the
+    chain rule; both plans keep their properties."""
+    kind, _, v = workload.split()
+    if kind == "lognormal":
+        c = W.LOGNORMAL
+        topk = np.array(W.lognormal_routing(c["R"], c["S"], c["E"], c["K"], float(v))[0])
+        R, E, C = c["R"], c["E"], c["S"] * c["K"]
+    else:
+        cfg = W.CONFIGS["skew"].with_(maxvio=float(v))
+        topk, _, _ = W.routing_for(cfg)
+        R, E, C = cfg.R, cfg.E, cfg.C
+    lo = O.make_plan(topk, E, 4, rule="lowmig")
+    ch = O.make_plan(topk, E, 4)
+    _plan_props(topk, lo, O.destinations(topk, lo))
+    mig_lo = sum(en.a for en in lo.entries)
+    mig_ch = sum(en.a for en in ch.entries)
+    assert mig_lo == O.min_migration_milp(lo.L, R, E, C)
+    assert mig_lo < mig_ch
 
 
 # ----------------------------------------------------------------------------
@@ -320,6 +375,8 @@ def test_lognormal_plan_properties(sigma):
     topk = np.array(topk)
     plan = O.make_plan(topk, c["E"], 4)
     _plan_props(topk, plan, O.destinations(topk, plan))
+    low = O.make_plan(topk, c["E"], 4, rule="lowmig")
+    _plan_props(topk, low, O.destinations(topk, low))
     st = O.stats_vector(plan)
     P = np.bincount(topk.ravel(), minlength=c["E"]).reshape(c["R"], -1).sum(axis=1)
     assert st[8] == P.max() and st[9] == P.min()      # baseline (home-pinned) rank loads
