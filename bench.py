@@ -14,6 +14,7 @@ TFLOP/s, a maxvio sweep, per-call rooflines, and the CPU oracle on a bounded sam
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import platform
@@ -366,6 +367,9 @@ def main():
                    for n in (1, 8, 64)},
         "re_prefetch_ms_per_layer": round(ms["prefetch"], 4),
     }
+    if not args.no_sweep:
+        pool["measured"] = measured_stack_peaks(torch, M, W, MoonEPLayer, MoonEPPool, stack_slot_bytes,
+                                                cfg, dev, log)
 
     # ---- practical HBM ceilings on this GPU (context only: 8 TB/s stays the denominator) ------
     # the library's weight prefetch is a plain 16-byte copy; torch's copy and fill show what the
@@ -432,6 +436,55 @@ def main():
     }
     print(json.dumps(out), flush=True)
     return 0
+
+
+def measured_stack_peaks(torch, M, W, MoonEPLayer, MoonEPPool, stack_slot_bytes, cfg, dev, log,
+                         depths=(1, 2, 4)):
+    """Device memory peak of a training stack of n layers (forward through all, backward in
+    reverse), with one prefetch pool for all layers or slots and reduce buffers per layer.
+    Measured with torch's allocator statistics at a shape whose per-layer buffers are small
+    (E=16 experts, S=512 tokens per rank) while the slots and reduce buffers keep their full
+    size (R, B, H, I as the benchmarked layer), so the pool is what the depth changes."""
+    R, B, H, I, K = cfg.R, cfg.B, cfg.H, cfg.I, cfg.K
+    E, S = 2 * R, 512
+    c = cfg.with_(E=E, S=S, lam=1.0, maxvio=None)
+    topk, gates, _ = W.routing_for(c)
+    tk, g = torch.from_numpy(topk).to(dev), torch.from_numpy(gates).to(dev)
+    x = torch.randn((R, S, H), device=dev).to(torch.bfloat16)
+    dout = torch.randn((R, S, H), device=dev).to(torch.bfloat16)
+    d = M.Dims.make(R, E, B, S, K, H, I, training=True)
+    out = {"shape": f"R{R} E{E} B{B} S{S} K{K} H{H} I{I}, training", "depths": {}}
+
+    def peak_of(n, pooled):
+        # everything the stack allocates is local to this call, so it is freed on return
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        p = MoonEPPool(R, B, H, I, training=True, device=dev) if pooled else None
+        stack = [MoonEPLayer(d, *W.expert_weights_torch(E, H, I, 50 + l, dev), training=True, pool=p)
+                 for l in range(n)]
+        h = x
+        for layer in stack:
+            h = layer.forward(h, tk, g).clone()
+        dh = dout
+        for layer in reversed(stack):
+            dh = layer.backward(dh, g).clone()
+        torch.cuda.synchronize()
+        return torch.cuda.max_memory_allocated() - base
+
+    for n in depths:
+        res = {}
+        for pooled in (True, False):
+            gc.collect()
+            torch.cuda.empty_cache()
+            res["pooled_peak_GB" if pooled else "per_layer_peak_GB"] = round(peak_of(n, pooled) / 1e9, 3)
+        res["measured_saving_GB"] = round(res["per_layer_peak_GB"] - res["pooled_peak_GB"], 3)
+        res["formula_saving_GB"] = round((stack_slot_bytes(R, B, H, I, n, False, True) -
+                                          stack_slot_bytes(R, B, H, I, n, True, True)) / 1e9, 3)
+        out["depths"][str(n)] = res
+        log("[bench] stack peak", n, res)
+    torch.cuda.empty_cache()
+    return out
 
 
 def algorithmic_work(cfg, st, cu, dst, topk):
