@@ -12,8 +12,9 @@
 //
 // Kernel design (MI355X / CDNA4):
 //   * 256x256 output tile per workgroup, 8 waves in 2x4 (two per SIMD), each wave
-//     128x64 = 4x2 tiles of v_mfma_f32_32x32x16_bf16 (bf16 inputs, fp32 accumulation);
-//     a 4-wave 2x2 layout of 128x128 per wave is a compile-time alternative.
+//     128x64 = 4x2 tiles of v_mfma_f32_32x32x16_bf16 (bf16 inputs, fp32 accumulation).
+//     Compile-time alternatives: a 4-wave 2x2 layout of 128x128 per wave for the row kernels;
+//     256x128 weight-gradient tiles on two 4-wave workgroups per CU.
 //   * Operand tiles go HBM -> LDS with global_load_lds_dwordx4 (16 bytes per lane, no
 //     register staging), addressed as a wave-uniform base in scalar registers plus a 32-bit
 //     per-lane offset.  Row kernels: 64-k stages in five 32 KiB buffers, one operand
@@ -56,9 +57,6 @@ constexpr int BM = 256, BN = 256, BK = 32, NSTAGE = 4;
 constexpr int OP_BYTES = 256 * BK * 2;             // one operand tile of one stage: 16 KiB
 constexpr int STAGE_BYTES = 2 * OP_BYTES;
 constexpr int GEMM_SMEM = NSTAGE * STAGE_BYTES;    // 128 KiB
-// weight-gradient kernel: the start of its epilogue staging (ring buffer 3 onwards, clear of the
-// next tile's first three steps)
-constexpr int DW_STG = 3 * STAGE_BYTES;
 // Row kernels: K step 64, so every k-contiguous row segment a DMA lane group fetches is one full
 // 128-byte line.
 constexpr int BK2 = 64;
@@ -171,15 +169,17 @@ __device__ __forceinline__ bf16x8_t frag_kc8(const char* T, int rb, int kk, int 
     const int r = rb + (lane & 31), c = kk * 2 + (lane >> 5);
     return *reinterpret_cast<const bf16x8_t*>(T + kc8_pos(r, c) * 16);
 }
-// same fragment from an m/n-contiguous tile: lane l gets column mb + l%32, k = 8*(l/32) + 0..7,
-// as two transposing reads of 4 k each (lanes of a 16-lane group address a 4 k x 16 col block)
+// same fragment from an m/n-contiguous tile of CH 16-byte chunks per k-row: lane l gets column
+// mb + l%32, k = 8*(l/32) + 0..7, as two transposing reads of 4 k each (lanes of a 16-lane group
+// address a 4 k x 16 col block)
+template <int CH = 32>
 __device__ __forceinline__ bf16x8_t frag_mn(const char* T, int mb, int kk, int lane) {
     const int G = lane >> 4, i = lane & 15;
     const int col = mb + 16 * (G & 1) + 4 * (i & 3);
     const int k = kk * 16 + 8 * (G >> 1) + (i >> 2);
-    const char* p = T + mn_pos(k, col >> 3) * 16 + (col & 7) * 2;
+    const char* p = T + (k * CH + ((col >> 3) ^ ((k & 3) << 2))) * 16 + (col & 7) * 2;
     const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
-    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p + 4 * 32 * 16));
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p + 4 * CH * 16));
     const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(bf16x8_t, v);
 }
@@ -214,15 +214,42 @@ struct Frags {
     bf16x8_t a[4], b[TN];
 };
 
+// Weight-gradient tiles: 256 (M) x TBN (N), waves of 128 x 64 in 2 x TBN/64.  TBN = 256: one
+// workgroup of 8 waves per CU, a ring of four 32-k stages.  TBN = 128: two workgroups of 4 waves
+// per CU (each wave has its own vmcnt, so one workgroup's output stores do not hold up the
+// other's copies), a ring of three stages each.
+template <int TBN>
+struct DWT {
+    static constexpr int WAVES = TBN / 32;
+    static constexpr int NTHR = 64 * WAVES;
+    static constexpr int WNN = TBN / 64;          // waves along N
+    static constexpr int TN = 2;                  // 32-column blocks per wave
+    static constexpr int NST = TBN == 256 ? 4 : 3;
+    static constexpr int OPA = 256 * BK * 2;      // A tile of one stage: [32 k][256 m]
+    static constexpr int OPB = TBN * BK * 2;      // B tile of one stage: [32 k][TBN n]
+    static constexpr int STAGE = OPA + OPB;
+    static constexpr int PA = 16 / WAVES;         // 1 KiB copies of A per wave and step
+    static constexpr int PB = (TBN / 16) / WAVES; // of B (PB <= PA)
+    static constexpr int PER = PA + PB;
+    static constexpr int BCH = TBN / 8;           // 16-byte chunks per k-row of the B tile
+    static constexpr int EPL = TN * 32 + 4;       // fp32 pitch of a staged epilogue row
+    // epilogue staging: the ring's last buffer onwards (the next tile's first NST-1 steps are
+    // in the others while this tile's results are stored)
+    static constexpr int STG = (NST - 1) * STAGE;
+    static constexpr int SMEM = NST * STAGE > STG + WAVES * 16 * EPL * 4 ? NST * STAGE
+                                                                          : STG + WAVES * 16 * EPL * 4;
+};
+static_assert(DWT<256>::SMEM <= ROWS_SMEM - 4096, "one 8-wave weight-gradient workgroup per CU");
+static_assert(2 * (DWT<128>::SMEM + 2048) <= ROWS_SMEM, "two 4-wave weight-gradient workgroups per CU");
+
 // Fragments of one 16-k slice of a weight-gradient step (both operands m/n-contiguous).
-template <int WN>
-__device__ __forceinline__ void load_frags(Frags<WL<WN>::TN>& f, const char* st, int kk, int wm, int wn, int lane) {
-    const char* As = st;
-    const char* Bs = st + OP_BYTES;
+template <int TBN>
+__device__ __forceinline__ void dw_load_frags(Frags<2>& f, const char* st, int kk, int wm, int wn, int lane) {
+    using T = DWT<TBN>;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) f.a[t] = frag_mn(As, wm * 128 + t * 32, kk, lane);
+    for (int t = 0; t < 4; ++t) f.a[t] = frag_mn<32>(st, wm * 128 + t * 32, kk, lane);
 #pragma unroll
-    for (int t = 0; t < WL<WN>::TN; ++t) f.b[t] = frag_mn(Bs, bcol<EPI_ACC_F32, WN>(wn, t), kk, lane);
+    for (int t = 0; t < 2; ++t) f.b[t] = frag_mn<T::BCH>(st + T::OPA, wn * 64 + t * 32, kk, lane);
 }
 
 template <int TN>
@@ -262,46 +289,51 @@ __device__ __forceinline__ void zero_acc(f32x16_t (&acc)[4][TN]) {
 
 // Weight-gradient main loop over nst K-steps of 32 (two 16-k slices each), split in two so a
 // persistent workgroup can issue the next tile's first copies before the current tile's stores.
-// issue(s, buf, part) enqueues this wave's DMA loads of step s (one per operand for part p,
-// p < PARTS) into a ring of NSTAGE buffers.  dw_prologue issues steps 0..NSTAGE-2.
-template <int WN, typename Issue>
+// issue(s, buf, part) enqueues this wave's DMA loads of step s (copy `part` of A, p < PA, and of
+// B if p < PB) into a ring of NST buffers.  dw_prologue issues steps 0..NST-2.
+template <int TBN, typename Issue>
 __device__ __forceinline__ void dw_prologue(int nst, Issue&& issue) {
+    using T = DWT<TBN>;
 #pragma unroll
-    for (int s = 0; s < NSTAGE - 1; ++s)
+    for (int s = 0; s < T::NST - 1; ++s)
         if (s < nst)
 #pragma unroll
-            for (int p = 0; p < WL<WN>::PARTS; ++p) issue(s, s, p);
+            for (int p = 0; p < T::PA; ++p) issue(s, s, p);
 }
 
 // Fragments are double-buffered in registers: the reads of the next slice are issued before the
 // MFMAs of the current one; the step barrier sits between a step's two slices so the MFMAs already
-// issued keep the matrix cores busy across it; and the DMA loads of step s+3 are spread between the
-// MFMAs of the second slice, so no burst of memory instructions stalls the wave's in-order issue
-// while the matrix pipe drains.
-template <int WN, typename Issue, typename IssueFast, typename FastRun>
-__device__ __forceinline__ void dw_main(f32x16_t (&acc)[4][WL<WN>::TN], char* smem, int nst, int wm,
-                                        int wn, int lane, Issue&& issue, IssueFast&& issue_fast,
-                                        FastRun&& fast_run) {
-    using L = WL<WN>;
-    constexpr int PER = L::PER_STEP;
+// issued keep the matrix cores busy across it; and the DMA loads of step s+NST-1 are spread between
+// the MFMAs of the second slice, so no burst of memory instructions stalls the wave's in-order
+// issue while the matrix pipe drains.
+template <int TBN, typename Issue, typename IssueFast, typename FastRun>
+__device__ __forceinline__ void dw_main(f32x16_t (&acc)[4][2], char* smem, int nst, int wm, int wn, int lane,
+                                        Issue&& issue, IssueFast&& issue_fast, FastRun&& fast_run) {
+    using T = DWT<TBN>;
+    constexpr int NST = T::NST, PER = T::PER;
     if (nst > 0) {
         // step 0 landed (vmcnt retires in issue order: all but the last n issued are done);
-        // steps 1 and 2 (if any) may still be in flight
-        if (nst >= 3) wait_vm<2 * PER>();
-        else if (nst == 2) wait_vm<PER>();
-        else wait_vm<0>();
+        // the following steps of the prologue (if any) may still be in flight
+        if constexpr (NST == 4) {
+            if (nst >= 3) wait_vm<2 * PER>();
+            else if (nst == 2) wait_vm<PER>();
+            else wait_vm<0>();
+        } else {
+            if (nst >= 2) wait_vm<PER>();
+            else wait_vm<0>();
+        }
         block_sync();
-        Frags<L::TN> f0, f1;
-        load_frags<WN>(f0, smem, 0, wm, wn, lane);
-        // One step.  FAST: a step s in 2 .. nst-4 (step s+3 exists) whose step s+3 is full and
-        // does not end its segment; the conditions are then compile-time, so these steps carry no
-        // branch around their waits and copies.  (Steps 0 and 1 run the general way: starting
-        // the fast run at step 0 measured the same.)
+        Frags<2> f0, f1;
+        dw_load_frags<TBN>(f0, smem, 0, wm, wn, lane);
+        // One step.  FAST: a step s in 2 .. nst-NST (step s+NST-1 exists) whose step s+NST-1 is
+        // full and does not end its segment; the conditions are then compile-time, so these steps
+        // carry no branch around their waits and copies.  (Steps 0 and 1 run the general way:
+        // starting the fast run at step 0 measured the same.)
         auto step = [&](int s, auto fast_c) {
             constexpr bool fast = decltype(fast_c)::value;
-            const char* st = smem + (s & (NSTAGE - 1)) * STAGE_BYTES;
-            load_frags<WN>(f1, st, 1, wm, wn, lane);
-            mma_frags<L::TN>(acc, f0);
+            const char* st = smem + ((unsigned)s % NST) * T::STAGE;
+            dw_load_frags<TBN>(f1, st, 1, wm, wn, lane);
+            mma_frags<2>(acc, f0);
             // Settle the slice-1 reads only after all slice-0 MFMAs are issued (the scheduling
             // barrier keeps the compiler from hoisting the wait above them, which would expose the
             // reads' latency); settling them here keeps the compiler from making the next MFMAs
@@ -309,22 +341,26 @@ __device__ __forceinline__ void dw_main(f32x16_t (&acc)[4][WL<WN>::TN], char* sm
             __builtin_amdgcn_sched_barrier(0);
             wait_lgkm0();
             if (fast || s + 1 < nst) {
-                // step s+1 must have landed; step s+2 may still be in flight
-                if (fast || s + 2 < nst) wait_vm<PER>();
-                else wait_vm<0>();
+                // step s+1 must have landed; with four stages step s+2 may still be in flight
+                if constexpr (NST == 4) {
+                    if (fast || s + 2 < nst) wait_vm<PER>();
+                    else wait_vm<0>();
+                } else {
+                    wait_vm<0>();
+                }
                 block_sync();
-                load_frags<WN>(f0, smem + ((s + 1) & (NSTAGE - 1)) * STAGE_BYTES, 0, wm, wn, lane);
+                dw_load_frags<TBN>(f0, smem + ((unsigned)(s + 1) % NST) * T::STAGE, 0, wm, wn, lane);
             }
-            // every wave is past step s-1, so its buffer takes step s+3
-            const bool more = fast || s + NSTAGE - 1 < nst;
-            const int nb = (s + NSTAGE - 1) & (NSTAGE - 1);
+            // every wave is past step s-1, so its buffer takes step s+NST-1
+            const bool more = fast || s + NST - 1 < nst;
+            const int nb = (unsigned)(s + NST - 1) % NST;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                mma_row<L::TN>(acc, f1, i);
-                if (more && i % (4 / L::PARTS) == 0) {
+                mma_row<2>(acc, f1, i);
+                if (more && i % (4 / T::PA) == 0) {
                     __builtin_amdgcn_sched_barrier(0);
-                    if constexpr (fast) issue_fast(s + NSTAGE - 1, nb, i / (4 / L::PARTS));
-                    else issue(s + NSTAGE - 1, nb, i / (4 / L::PARTS));
+                    if constexpr (fast) issue_fast(s + NST - 1, nb, i / (4 / T::PA));
+                    else issue(s + NST - 1, nb, i / (4 / T::PA));
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -333,11 +369,11 @@ __device__ __forceinline__ void dw_main(f32x16_t (&acc)[4][WL<WN>::TN], char* sm
         for (; s < nst && s < 2; ++s) step(s, std::false_type{});
         // the run of full steps that the cursor's segment still holds (all of a one-segment
         // target's steps but its last), then everything else the general way
-        if (s + NSTAGE - 1 < nst) {
-            const int e = s + max(0, min(nst - (NSTAGE - 1) - s, fast_run()));
+        if (s + NST - 1 < nst) {
+            const int e = s + max(0, min(nst - (NST - 1) - s, fast_run()));
             for (; s < e; ++s) step(s, std::true_type{});
         }
-        for (; s + NSTAGE - 1 < nst; ++s) step(s, std::false_type{});
+        for (; s + NST - 1 < nst; ++s) step(s, std::false_type{});
         for (; s < nst; ++s) step(s, std::false_type{});
     }
     block_sync();     // every wave is done with the ring before the next tile's copies reuse it
@@ -618,15 +654,15 @@ __device__ __forceinline__ void stage_half(const f32x16_t (&acc)[4][TN], float* 
 // Weight-gradient epilogue for rows 16h..16h+15 of row block q: float32 stores, or += with
 // MOONEP_GRAD_ACCUM.  FULL: the tile lies inside [M, N], so every store is issued unmasked and
 // the caller can count them.
-template <int WN, int q, int h, bool FULL>
-__device__ __forceinline__ void epi_dw_part(const GemmArgs& a, const f32x16_t (&acc)[4][WL<WN>::TN], float* ep,
+template <int q, int h, bool FULL>
+__device__ __forceinline__ void epi_dw_part(const GemmArgs& a, const f32x16_t (&acc)[4][2], float* ep,
                                             int wm, int wn, int lane, float* out, int m0, int n0) {
-    constexpr int TN = WL<WN>::TN, EPLD = WL<WN>::EPL;
+    constexpr int TN = 2, EPLD = TN * 32 + 4;
     constexpr int LPR = 8 * TN, RPI = 64 / LPR, IT = 16 / RPI;   // float4 chunks
     stage_half<q, h, TN, EPLD>(acc, ep, lane);
     wave_sync();
     const int c = (lane % LPR) * 4;
-    const int col = n0 + wn * (256 / WN) + c;
+    const int col = n0 + wn * 64 + c;
     const int rb = m0 + wm * 128 + q * 32 + h * 16;
     if (!a.accum) {
 #pragma unroll
@@ -666,17 +702,17 @@ __device__ __forceinline__ void epi_dw_part(const GemmArgs& a, const f32x16_t (&
     wave_sync();
 }
 
-template <int WN, bool FULL>
-__device__ __forceinline__ void epi_dw(const GemmArgs& a, const f32x16_t (&acc)[4][WL<WN>::TN], float* ep, int wm,
+template <bool FULL>
+__device__ __forceinline__ void epi_dw(const GemmArgs& a, const f32x16_t (&acc)[4][2], float* ep, int wm,
                                        int wn, int lane, float* out, int m0, int n0) {
-    epi_dw_part<WN, 0, 0, FULL>(a, acc, ep, wm, wn, lane, out, m0, n0);
-    epi_dw_part<WN, 0, 1, FULL>(a, acc, ep, wm, wn, lane, out, m0, n0);
-    epi_dw_part<WN, 1, 0, FULL>(a, acc, ep, wm, wn, lane, out, m0, n0);
-    epi_dw_part<WN, 1, 1, FULL>(a, acc, ep, wm, wn, lane, out, m0, n0);
-    epi_dw_part<WN, 2, 0, FULL>(a, acc, ep, wm, wn, lane, out, m0, n0);
-    epi_dw_part<WN, 2, 1, FULL>(a, acc, ep, wm, wn, lane, out, m0, n0);
-    epi_dw_part<WN, 3, 0, FULL>(a, acc, ep, wm, wn, lane, out, m0, n0);
-    epi_dw_part<WN, 3, 1, FULL>(a, acc, ep, wm, wn, lane, out, m0, n0);
+    epi_dw_part<0, 0, FULL>(a, acc, ep, wm, wn, lane, out, m0, n0);
+    epi_dw_part<0, 1, FULL>(a, acc, ep, wm, wn, lane, out, m0, n0);
+    epi_dw_part<1, 0, FULL>(a, acc, ep, wm, wn, lane, out, m0, n0);
+    epi_dw_part<1, 1, FULL>(a, acc, ep, wm, wn, lane, out, m0, n0);
+    epi_dw_part<2, 0, FULL>(a, acc, ep, wm, wn, lane, out, m0, n0);
+    epi_dw_part<2, 1, FULL>(a, acc, ep, wm, wn, lane, out, m0, n0);
+    epi_dw_part<3, 0, FULL>(a, acc, ep, wm, wn, lane, out, m0, n0);
+    epi_dw_part<3, 1, FULL>(a, acc, ep, wm, wn, lane, out, m0, n0);
 }
 
 // ---------------------------------------------------------------------------
@@ -826,25 +862,22 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_rows_kernel(GemmArgs a) {
 // issued all of them without pacing measured 1-2% slower; the compiled epilogue also waits for
 // the previous slice's stores before each slice (a side effect of the accumulate path's loads),
 // and wave 0 for all of its operations after the tile counter's atomic add.
-template <int WN>
-constexpr int dw_smem() { return DW_STG + WL<WN>::WAVES * 16 * WL<WN>::EPL * 4; }
-static_assert(dw_smem<2>() <= ROWS_SMEM - 4096 && dw_smem<4>() <= ROWS_SMEM - 4096,
-              "weight-gradient staging plus the kernel's static LDS must fit in 160 KiB");
-
-template <int WN, int WHICH>
-__global__ __launch_bounds__(128 * WN, 1) void gemm_dw_kernel(GemmArgs a) {
-    using L = WL<WN>;
+template <int TBN, int WHICH>
+__global__ __launch_bounds__(DWT<TBN>::NTHR, TBN == 128 ? 2 : 1) void gemm_dw_kernel(GemmArgs a) {
+    using T = DWT<TBN>;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     __shared__ Segment s_seg[2][kMaxR + 1];
     __shared__ int s_tile[2];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / WN, wn = wave % WN;
+    const int wm = wave / T::WNN, wn = wave % T::WNN;
     const PlanWs& w = a.w;
     const int MT = (a.M + BM - 1) / BM, NT = a.ntiles_n;
     const int per_target = MT * NT;
     const int total = (w.E + w.R * w.B) * per_target;
-    float* ep = reinterpret_cast<float*>(smem + DW_STG) + wave * 16 * L::EPL;
-    const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds_addr(smem) + wave * L::PARTS * 1024);
+    float* ep = reinterpret_cast<float*>(smem + T::STG) + wave * 16 * T::EPL;
+    // this wave's 1 KiB DMA slots of the A and B tiles of a stage
+    const uint32_t lds_a = __builtin_amdgcn_readfirstlane(lds_addr(smem) + wave * T::PA * 1024);
+    const uint32_t lds_b = __builtin_amdgcn_readfirstlane(lds_addr(smem) + T::OPA + wave * T::PB * 1024);
 
     // Tile ids pass through s_tile, alternating between its two words, so a wave still reading
     // one word is never overtaken by thread 0 writing the next id into it.
@@ -896,7 +929,7 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_dw_kernel(GemmArgs a) {
         nst = 0;
         for (int i = 0; i < nseg; ++i) nst += (s_seg[par][i].rows + BK - 1) / BK;
         m0 = mt * BM;
-        n0 = nt * BN;
+        n0 = nt * TBN;
         // (an expert without rows gets a zero gradient when the outputs are written)
         return nst > 0 || !a.accum;
     };
@@ -905,15 +938,20 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_dw_kernel(GemmArgs a) {
     // load (k-row kk of the step, a 16-byte column chunk) from the step's first row, and a cursor
     // over the segments; columns outside the tile clamp to the last valid chunk (their products
     // only reach outputs the epilogue does not store), rows past a segment's end load zeros
-    uint32_t ao[L::PARTS], bo[L::PARTS];
+    uint32_t ao[T::PA], bo[T::PB];
     int ipar = 0, iseg = 0, ikoff = 0;
     Segment icur{0, 0};
     auto start_issue = [&](int par) {
 #pragma unroll
-        for (int i = 0; i < L::PARTS; ++i) {
-            const int p = (wave * L::PARTS + i) * 64 + lane;
+        for (int i = 0; i < T::PA; ++i) {
+            const int p = (wave * T::PA + i) * 64 + lane;
             const int k = p >> 5, c = (p & 31) ^ ((k & 3) << 2);
             ao[i] = 2u * (uint32_t)(k * a.lda + min(m0 + c * 8, a.M - 8));
+        }
+#pragma unroll
+        for (int i = 0; i < T::PB; ++i) {
+            const int p = (wave * T::PB + i) * 64 + lane;
+            const int k = p / T::BCH, c = (p % T::BCH) ^ ((k & 3) << 2);
             bo[i] = 2u * (uint32_t)(k * a.ldb + min(n0 + c * 8, a.N - 8));
         }
         ipar = par;
@@ -923,20 +961,24 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_dw_kernel(GemmArgs a) {
         icur = iseg < nseg ? s_seg[par][iseg] : Segment{0, 0};
     };
     auto issue = [&](int, int buf, int i) {
-        const uint32_t l = lds_wave + buf * STAGE_BYTES + i * 1024;
+        const uint32_t la = __builtin_amdgcn_readfirstlane(lds_a + buf * T::STAGE + i * 1024);
+        const uint32_t lb = __builtin_amdgcn_readfirstlane(lds_b + buf * T::STAGE + i * 1024);
         const int row = __builtin_amdgcn_readfirstlane(icur.row0 + ikoff);
         const int left = __builtin_amdgcn_readfirstlane(icur.rows - ikoff);
         const uint16_t* ga = a.A + (size_t)row * a.lda;
         const uint16_t* gb = a.B + (size_t)row * a.ldb;
         if (__builtin_expect(left >= BK, 1)) {   // all but a segment's last step: fall-through path
-            dma16s(ga, ao[i], l);
-            dma16s(gb, bo[i], l + OP_BYTES);
-        } else {    // k-row of this lane's load: ((wave * PARTS + i) * 64 + lane) / 32
-            const bool v = (wave * L::PARTS + i) * 2 + (lane >> 5) < left;
-            dma16(v ? ga + ao[i] / 2 : w.zeros, l);
-            dma16(v ? gb + bo[i] / 2 : w.zeros, l + OP_BYTES);
+            dma16s(ga, ao[i], la);
+            if (i < T::PB) dma16s(gb, bo[i], lb);
+        } else {    // rows past the segment's end load zeros; k-row of the lane's copy as in start_issue
+            const bool va = (((wave * T::PA + i) * 64 + lane) >> 5) < left;
+            dma16(va ? ga + ao[i] / 2 : w.zeros, la);
+            if (i < T::PB) {
+                const bool vb = ((wave * T::PB + i) * 64 + lane) / T::BCH < left;
+                dma16(vb ? gb + bo[i] / 2 : w.zeros, lb);
+            }
         }
-        if (i == L::PARTS - 1) {    // step issued: advance the cursor
+        if (i == T::PA - 1) {    // step issued: advance the cursor
             ikoff += BK;
             if (__builtin_expect(ikoff >= icur.rows, 0)) {
                 // next segment with rows: an empty one (a descriptor a valid plan never makes)
@@ -950,11 +992,11 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_dw_kernel(GemmArgs a) {
     };
     // A full step that does not end its segment (more than BK rows left): no branches.
     auto issue_fast = [&](int, int buf, int i) {
-        const uint32_t l = lds_wave + buf * STAGE_BYTES + i * 1024;
         const int row = __builtin_amdgcn_readfirstlane(icur.row0 + ikoff);
-        dma16s(a.A + (size_t)row * a.lda, ao[i], l);
-        dma16s(a.B + (size_t)row * a.ldb, bo[i], l + OP_BYTES);
-        if (i == L::PARTS - 1) ikoff += BK;
+        dma16s(a.A + (size_t)row * a.lda, ao[i], __builtin_amdgcn_readfirstlane(lds_a + buf * T::STAGE + i * 1024));
+        if (i < T::PB)
+            dma16s(a.B + (size_t)row * a.ldb, bo[i], __builtin_amdgcn_readfirstlane(lds_b + buf * T::STAGE + i * 1024));
+        if (i == T::PA - 1) ikoff += BK;
     };
     // how many steps issue_fast may issue in a row from the cursor
     auto fast_run = [&]() { return __builtin_amdgcn_readfirstlane((icur.rows - ikoff - 1) / BK); };
@@ -966,15 +1008,15 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_dw_kernel(GemmArgs a) {
     while (t < total && !(have = setup(t, 0))) t = fetch();
     if (have) {
         start_issue(0);
-        dw_prologue<WN>(nst, issue);
+        dw_prologue<TBN>(nst, issue);
     }
     while (have) {
         int nxt = 0;
         if (tid == 0) nxt = atomicAdd(a.counter, 1);   // consumed after the main loop (an atomic
                                                        // add on purpose: see the loop's header)
-        f32x16_t acc[4][L::TN];
-        zero_acc<L::TN>(acc);
-        dw_main<WN>(acc, smem, nst, wm, wn, lane, issue, issue_fast, fast_run);
+        f32x16_t acc[4][2];
+        zero_acc<2>(acc);
+        dw_main<TBN>(acc, smem, nst, wm, wn, lane, issue, issue_fast, fast_run);
         // this tile's output, kept while the next tile is set up
         float* const cout = out;
         const int cm0 = m0, cn0 = n0;
@@ -984,12 +1026,12 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_dw_kernel(GemmArgs a) {
         while (tn < total && !(next = setup(tn, par ^ 1))) tn = fetch();
         if (next) {
             start_issue(par ^ 1);
-            dw_prologue<WN>(nst, issue);
+            dw_prologue<TBN>(nst, issue);
         }
         // this tile's stores (unmasked for an interior tile), all retired before the next tile
-        const bool full = cm0 + BM <= a.M && cn0 + BN <= a.N;
-        if (full) epi_dw<WN, true>(a, acc, ep, wm, wn, lane, cout, cm0, cn0);
-        else epi_dw<WN, false>(a, acc, ep, wm, wn, lane, cout, cm0, cn0);
+        const bool full = cm0 + BM <= a.M && cn0 + TBN <= a.N;
+        if (full) epi_dw<true>(a, acc, ep, wm, wn, lane, cout, cm0, cn0);
+        else epi_dw<false>(a, acc, ep, wm, wn, lane, cout, cm0, cn0);
         wait_vm<0>();
         have = next;
         par ^= 1;
@@ -1057,9 +1099,12 @@ static bool set_smem(K kernel, int bytes) {
 #ifndef MOONEP_WN_ROWS
 #define MOONEP_WN_ROWS 4
 #endif
-#ifndef MOONEP_WN_DW
-#define MOONEP_WN_DW 4
+// weight-gradient tile width: 256 (one 8-wave workgroup per CU) or 128 (two 4-wave workgroups)
+#ifndef MOONEP_DW_TBN
+#define MOONEP_DW_TBN 256
 #endif
+constexpr int DW_TBN = MOONEP_DW_TBN;
+static_assert(DW_TBN == 256 || DW_TBN == 128, "weight-gradient tile width");
 
 // Resets the eight per-XCD tile counters, then runs a row kernel.
 static int launch_rows(int epi, int mode, const GemmArgs& a0, hipStream_t s) {
@@ -1089,17 +1134,16 @@ static int launch_rows(int epi, int mode, const GemmArgs& a0, hipStream_t s) {
 // weight-gradient kernel.
 template <int WHICH>
 static int launch_dw(const GemmArgs& a, hipStream_t s) {
-    constexpr int WN = MOONEP_WN_DW;
-    constexpr int smem = dw_smem<WN>();
-    static bool ok = set_smem(gemm_dw_kernel<WN, WHICH>, smem);
+    constexpr int smem = DWT<DW_TBN>::SMEM;
+    static bool ok = set_smem(gemm_dw_kernel<DW_TBN, WHICH>, smem);
     if (!ok) return MOONEP_EHIP;
     const size_t okey_bytes = (size_t)(a.w.E + a.w.R * a.w.B) * sizeof(unsigned long long);
     static bool ok_order = set_smem(dw_prepare_kernel, (int)((kMaxE + kMaxR * kMaxB) * sizeof(unsigned long long)));
     if (!ok_order) return MOONEP_EHIP;
     hipLaunchKernelGGL(dw_prepare_kernel, dim3(1), dim3(kOrderThreads), okey_bytes, s, a.w, a.counter);
     MOONEP_LAUNCH_CHECK();
-    const int grid = (num_cus() / 8) * 8;
-    hipLaunchKernelGGL((gemm_dw_kernel<WN, WHICH>), dim3(grid), dim3(128 * WN), smem, s, a);
+    const int grid = (num_cus() / 8) * 8 * (DW_TBN == 128 ? 2 : 1);
+    hipLaunchKernelGGL((gemm_dw_kernel<DW_TBN, WHICH>), dim3(grid), dim3(DWT<DW_TBN>::NTHR), smem, s, a);
     MOONEP_LAUNCH_CHECK();
     return MOONEP_OK;
 }
@@ -1263,7 +1307,7 @@ extern "C" int moonep_grouped_ffn_backward(const moonep_dims_t* dims, const void
     d.N = H;
     d.dw_home = dw2_home;
     d.dw_slot = dw2_red;
-    d.ntiles_n = (H + BN - 1) / BN;
+    d.ntiles_n = (H + DW_TBN - 1) / DW_TBN;
     d.counter = a.w.counters;
     d.accum = (dims->flags & MOONEP_GRAD_ACCUM) ? 1 : 0;
     if (ph & MOONEP_PHASE_DW2) {
@@ -1279,7 +1323,7 @@ extern "C" int moonep_grouped_ffn_backward(const moonep_dims_t* dims, const void
     d.N = 2 * I;
     d.dw_home = dw13_home;
     d.dw_slot = dw13_red;
-    d.ntiles_n = (2 * I + BN - 1) / BN;
+    d.ntiles_n = (2 * I + DW_TBN - 1) / DW_TBN;
     d.counter = a.w.counters + 1;
     return (ph & MOONEP_PHASE_DW13) ? launch_dw<13>(d, s) : MOONEP_OK;
 }
