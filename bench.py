@@ -43,8 +43,8 @@ KERNEL_NAMES = {
     "dispatch_bwd": "moonep::dispatch_kernel<false, true, 8, 2, false, true>",
     "gemm_dact": "moonep::gemm_rows_kernel<1, 2, 4>",
     "gemm_dx": "moonep::gemm_rows_kernel<1, 1, 4>",
-    "gemm_dw2": "moonep::gemm_dw_kernel<4, 2>",
-    "gemm_dw13": "moonep::gemm_dw_kernel<4, 13>",
+    "gemm_dw2": "moonep::gemm_dw_kernel<256, 2>",
+    "gemm_dw13": "moonep::gemm_dw_kernel<256, 13>",
     "combine_bwd": "moonep::combine_kernel<false, false, 7, false, false>",
     "reduce_grad": "moonep::reduce_grad_kernel",
 }
