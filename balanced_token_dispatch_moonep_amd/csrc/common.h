@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "../../include/moonep.h"
 
 namespace moonep {
@@ -16,6 +18,12 @@ constexpr int kMaxE = 1024;
 constexpr int kMaxG = 64;            // home experts per rank
 constexpr int kMaxB = 64;
 constexpr int kMaxK = 16;
+// chunks per planning histogram segment, at most (fewer segments: less for plan_decide to sum;
+// more: more workgroups for plan_hist)
+#ifndef MOONEP_PLAN_SEG
+#define MOONEP_PLAN_SEG 16
+#endif
+constexpr int kSegMax = MOONEP_PLAN_SEG;
 constexpr int kZeroElems = 512;      // zero bf16 elements kept in the plan workspace
 constexpr uint32_t kFwdPhases = MOONEP_PHASE_GATE_UP | MOONEP_PHASE_DOWN;
 constexpr uint32_t kBwdPhases = MOONEP_PHASE_DACT | MOONEP_PHASE_DX | MOONEP_PHASE_DW2 | MOONEP_PHASE_DW13;
@@ -48,11 +56,13 @@ struct Segment {
 // Plan workspace layout.  Every array is rewritten by each moonep_plan call before it is read.
 struct PlanWs {
     int R, E, B, S, K, G, C, NC, NCH;
+    int SEG, NSEG;         // chunks per histogram segment (consecutive in (rank, token) order), segments
     int32_t* hdr;          // [HDR_WORDS]
     uint64_t* bm;          // [NCH][E]   bit t of bm[ch][e]: token t of chunk ch picked e
-    int32_t* cnt;          // [E][NCH]   per-chunk counts, then exclusive prefix (rank-major)
-    int32_t* chunk_status; // [NCH]
-    int32_t* L;            // [E]
+    int32_t* cnt;          // [NCH][E]   pairs of e in the earlier chunks of ch's segment
+    int32_t* segtot;       // [NSEG][E]  pairs of e in each segment
+    int32_t* segpre;       // [NSEG][E]  pairs of e in the earlier segments
+    int32_t* chunk_status; // [NSEG]     invalid / duplicate ids seen in each segment
     int32_t* keep;         // [E]
     int32_t* ninst;        // [E]
     int32_t* inst;         // [E][kMaxR][3]  (start g, rows, dest offset = q*C + cu - start)
@@ -82,6 +92,9 @@ inline size_t plan_ws_layout(const moonep_dims_t* d, void* base, PlanWs* ws) {
     w.G = d->E / d->R; w.C = d->S * d->K;
     w.NC = (d->S + kChunk - 1) / kChunk;
     w.NCH = w.R * w.NC;
+    // a segment's bitmaps fill at most 64 KiB of LDS
+    w.SEG = std::max(1, std::min(kSegMax, 8192 / w.E));
+    w.NSEG = (w.NCH + w.SEG - 1) / w.SEG;
     size_t off = 0;
     char* b = static_cast<char*>(base);
     auto take = [&](size_t bytes) -> void* {
@@ -93,8 +106,9 @@ inline size_t plan_ws_layout(const moonep_dims_t* d, void* base, PlanWs* ws) {
     w.hdr = (int32_t*)take(HDR_WORDS * 4);
     w.bm = (uint64_t*)take(NCH * E * 8);
     w.cnt = (int32_t*)take(NCH * E * 4);
-    w.chunk_status = (int32_t*)take(NCH * 4);
-    w.L = (int32_t*)take(E * 4);
+    w.segtot = (int32_t*)take((size_t)w.NSEG * E * 4);
+    w.segpre = (int32_t*)take((size_t)w.NSEG * E * 4);
+    w.chunk_status = (int32_t*)take((size_t)w.NSEG * 4);
     w.keep = (int32_t*)take(E * 4);
     w.ninst = (int32_t*)take(E * 4);
     w.inst = (int32_t*)take(E * kMaxR * 3 * 4);

@@ -7,23 +7,23 @@
 // The planner reads the router's top-K choices and decides, with no host
 // synchronisation, which experts get a temporary copy on which rank so that every
 // rank serves exactly C = S*K rows [TC, "What the technique is" and its flowchart;
-// TD, summary; AL, How it works].  Four launches:
+// TD, summary; AL, How it works].  Three launches:
 //
-//   plan_hist   one wave per 64-token chunk: an LDS bitmap per expert (bit t = token t of
-//               the chunk picked the expert), built with LDS atomic OR (order-free, so the
-//               result is deterministic); its popcounts are the chunk's expert counts.
-//               A bit already set flags a duplicate expert within a token.
-//   plan_scan   one wave per expert: exclusive prefix of the chunk counts in (rank, token)
-//               order with wave shuffles -> each chunk's first pair index per expert; the
-//               total is the expert's load L[e].
-//   plan_decide one workgroup: rank loads, donors/receivers, the duplicate chain with
+//   plan_hist   one workgroup per segment of up to 16 consecutive 64-token chunks (one wave
+//               per chunk, topk loads issued before the atomics): an LDS
+//               bitmap per chunk and expert (bit t = token t of the chunk picked the expert),
+//               built with LDS atomic OR (order-free, so the result is deterministic); per
+//               expert, the exclusive prefix of the chunk popcounts within the segment and the
+//               segment total.  A bit already set flags a duplicate expert within a token.
+//   plan_decide one workgroup: expert loads L[e] (sums of the segment totals) and each
+//               segment's offset per expert, rank loads, donors/receivers, the duplicate chain with
 //               best-fit picks done as wave-wide argmin/argmax (at most one remote home
 //               group per rank [TC, Installation and integration]), prefetch slots or
 //               home-row fallback [TD, memory contract], cu_seqlens per rank and weight
 //               row, instance offsets, GEMM group tables, the weight-gradient work order
 //               (targets by rows, descending) and statistics.
-//   plan_dest   one wave per chunk: pair index g = chunk prefix + popcount of the lower
-//               bits of the expert's bitmap; the instance holding g gives the final row
+//   plan_dest   one wave per chunk: pair index g = segment offset + prefix within the segment
+//               + popcount of the lower bits of the expert's bitmap; the instance holding g gives the final row
 //               (the send side computes the receiver's position [TC, "What the technique
 //               is"]).
 //
@@ -38,69 +38,77 @@ namespace moonep {
 
 constexpr int kBad = MOONEP_ST_BAD_ID | MOONEP_ST_DUP_ID | MOONEP_ST_CAPACITY | MOONEP_ST_OVERFLOW;
 
-__global__ __launch_bounds__(64) void plan_hist(const int32_t* __restrict__ topk, PlanWs w) {
-    extern __shared__ unsigned long long sbm[];   // [E]
-    const int ch = blockIdx.x;
-    const int r = ch / w.NC, c = ch % w.NC;
-    const int t = threadIdx.x;
-    for (int e = t; e < w.E; e += 64) sbm[e] = 0ull;
+// One workgroup per segment of SEG consecutive chunks (in (rank, token) order), one wave per
+// chunk (a wave takes chunks wave and wave + 16 of a 32-chunk segment, its topk loads for both
+// issued before either chunk's atomics): LDS bitmaps per chunk and expert (bit t = token t of the
+// chunk picked the expert), built with LDS atomic OR (order-free, so the result is
+// deterministic).  Then, per expert, the exclusive prefix of the popcounts over the segment's
+// chunks and the segment total.  A bit already set flags a duplicate expert within a token.
+constexpr int kHistThreads = 1024, kHistWaves = kHistThreads / 64;
+constexpr int kHistRounds = (kSegMax + kHistWaves - 1) / kHistWaves;
+__global__ __launch_bounds__(kHistThreads) void plan_hist(const int32_t* __restrict__ topk, PlanWs w) {
+    extern __shared__ unsigned long long sbm[];   // [SEG][E]
+    __shared__ int sst;
+    const int seg = blockIdx.x;
+    const int ch0 = seg * w.SEG, nch = min(w.SEG, w.NCH - ch0);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int E = w.E, K = w.K;
+    for (int i = tid; i < nch * E; i += kHistThreads) sbm[i] = 0ull;
+    if (tid == 0) sst = 0;
+    // this wave's chunks: the ids of its tokens' picks, all loads in flight together
+    int ev[kHistRounds][kMaxK];
+#pragma unroll
+    for (int rd = 0; rd < kHistRounds; ++rd) {
+        const int cl = wave + rd * kHistWaves;
+        const int ch = ch0 + cl;
+        const int r = ch / w.NC, c = ch % w.NC;
+        const int s = c * kChunk + lane;
+        const bool on = cl < nch && s < w.S;
+        const int32_t* tp = on ? topk + ((size_t)r * w.S + s) * K : topk;
+#pragma unroll
+        for (int k = 0; k < kMaxK; ++k) ev[rd][k] = on && k < K ? tp[k] : -1;
+    }
     __syncthreads();
-    const int s = c * kChunk + t;
     int st = 0;
-    if (s < w.S) {
-        const int32_t* tp = topk + ((size_t)r * w.S + s) * w.K;
-        for (int k = 0; k < w.K; ++k) {
-            const int e = tp[k];
-            if ((unsigned)e >= (unsigned)w.E) {
+#pragma unroll
+    for (int rd = 0; rd < kHistRounds; ++rd) {
+        const int cl = wave + rd * kHistWaves;
+        const int s = ((ch0 + cl) % w.NC) * kChunk + lane;
+        if (cl >= nch || s >= w.S) continue;
+#pragma unroll
+        for (int k = 0; k < kMaxK; ++k) {
+            if (k >= K) break;
+            const int e = ev[rd][k];
+            if ((unsigned)e >= (unsigned)E) {
                 st |= MOONEP_ST_BAD_ID;
                 continue;
             }
-            const unsigned long long old = atomicOr(&sbm[e], 1ull << t);
-            if ((old >> t) & 1ull) st |= MOONEP_ST_DUP_ID;
+            const unsigned long long old = atomicOr(&sbm[cl * E + e], 1ull << lane);
+            if ((old >> lane) & 1ull) st |= MOONEP_ST_DUP_ID;
         }
     }
-    const unsigned long long bad = __ballot(st & MOONEP_ST_BAD_ID);
-    const unsigned long long dup = __ballot(st & MOONEP_ST_DUP_ID);
+    if (st) atomicOr(&sst, st);
     __syncthreads();
-    for (int e = t; e < w.E; e += 64) {
-        const unsigned long long b = sbm[e];
-        w.bm[(size_t)ch * w.E + e] = b;
-        w.cnt[(size_t)e * w.NCH + ch] = __popcll(b);
-    }
-    if (t == 0) w.chunk_status[ch] = (bad ? MOONEP_ST_BAD_ID : 0) | (dup ? MOONEP_ST_DUP_ID : 0);
-}
-
-// Exclusive prefix of each expert's chunk counts in (rank, token) order, one wave per expert.
-// The counts are loaded eight 64-chunk batches at a time before they are scanned, so the loads
-// of a batch are in flight together rather than one after another.
-constexpr int kScanBatch = 8;
-__global__ __launch_bounds__(256) void plan_scan(PlanWs w) {
-    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    if (e >= w.E) return;
-    int32_t* row = w.cnt + (size_t)e * w.NCH;
-    int run = 0;
-    for (int base = 0; base < w.NCH; base += 64 * kScanBatch) {
-        int v[kScanBatch];
+    // per expert: the segment's bitmaps read eight chunks at a time, then written out with the
+    // running prefix
+    for (int e = tid; e < E; e += kHistThreads) {
+        int run = 0;
+        for (int c0 = 0; c0 < nch; c0 += 8) {
+            unsigned long long bv[8];
 #pragma unroll
-        for (int b = 0; b < kScanBatch; ++b) {
-            const int i = base + b * 64 + lane;
-            v[b] = i < w.NCH ? row[i] : 0;
-        }
+            for (int b = 0; b < 8; ++b) bv[b] = c0 + b < nch ? sbm[(c0 + b) * E + e] : 0ull;
 #pragma unroll
-        for (int b = 0; b < kScanBatch; ++b) {
-            int x = v[b];
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const int y = __shfl_up(x, o, 64);
-                if (lane >= o) x += y;
+            for (int b = 0; b < 8; ++b) {
+                if (c0 + b >= nch) break;
+                const size_t o = (size_t)(ch0 + c0 + b) * E + e;
+                w.bm[o] = bv[b];
+                w.cnt[o] = run;
+                run += __popcll(bv[b]);
             }
-            const int i = base + b * 64 + lane;
-            if (i < w.NCH) row[i] = run + x - v[b];
-            run += __shfl(x, 63, 64);
         }
+        w.segtot[(size_t)seg * E + e] = run;
     }
-    if (lane == 0) w.L[e] = run;
+    if (tid == 0) w.chunk_status[seg] = sst;
 }
 
 // Wave-wide min / max of a 32-bit value: DPP exchanges inside each row of 16 lanes (quad
@@ -116,14 +124,56 @@ __device__ __forceinline__ int wave_reduce(int v) {
               op(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
 
+// Wave-wide sum, the same exchanges as wave_reduce.  Every lane must be active.
+__device__ __forceinline__ int wave_sum(int v) {
+    v += __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);
+    v += __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);
+    v += __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false);
+    v += __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, false);
+    return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+           (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
+}
+
+// Wave-wide unsigned minimum, the same exchanges as wave_reduce.
+__device__ __forceinline__ unsigned wave_reduce_u32(unsigned v) {
+    auto mn = [](unsigned a, unsigned b) { return a < b ? a : b; };
+    v = mn(v, (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));
+    v = mn(v, (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));
+    v = mn(v, (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));
+    v = mn(v, (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));
+    return mn(mn((unsigned)__builtin_amdgcn_readlane((int)v, 0), (unsigned)__builtin_amdgcn_readlane((int)v, 16)),
+              mn((unsigned)__builtin_amdgcn_readlane((int)v, 32), (unsigned)__builtin_amdgcn_readlane((int)v, 48)));
+}
+
 // lowest lane whose flag is set (flags wave-uniformly nonzero)
 __device__ __forceinline__ int first_lane(bool f) {
     return __builtin_ctzll(__ballot(f));
 }
 
+// Workgroup barrier for LDS data only: waits for this wave's LDS operations, not for its global
+// stores (which __syncthreads' fence would wait for; no phase of plan_decide reads what an earlier
+// one stored to global memory).
+__device__ __forceinline__ void lds_sync() {
+    __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));   // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Wave barrier for a data exchange between the lanes of one wave through LDS: this wave's LDS
+// operations complete, and the compiler moves no memory access across it.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));   // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Per-expert replica counters, packed: all replicas (bits 0-9), slot replicas (10-19),
 // fallback replicas (20-29).  An expert has at most R - 1 < 1024 replicas.
 constexpr int kCntAll = 1, kCntSlot = 1 << 10, kCntFb = 1 << 20;
+
+constexpr int kDecideThreadsMax = 512;
 
 struct DecideShared {
     int L[kMaxE];                 // rows routed to each expert
@@ -143,8 +193,8 @@ struct DecideShared {
     int hometot[kMaxR];           // rows kept by each rank's home group
     int nzbase[kMaxR + 1];        // experts that keep rows in the home groups before each rank
     int P[kMaxR], X[kMaxR], don[kMaxR], rec[kMaxR];
-    int nd, nr, nent, status, nred;
-    int migr, nslot, nfb, fbrows, maxl;
+    int lpart[kDecideThreadsMax];  // partial expert loads (segments split over threads)
+    int nent, status;
 };
 
 // Rows on rank q whose weight row is below w, i.e. cu_seqlens[q][w] (home rows in expert order,
@@ -157,7 +207,7 @@ __device__ __forceinline__ int cu_at(const DecideShared& sh, int q, int w, int E
     return s;
 }
 
-constexpr int kDecideThreads = 512;
+constexpr int kDecideThreads = kDecideThreadsMax;
 
 __global__ __launch_bounds__(kDecideThreads) void plan_decide(PlanWs w, uint32_t flags, int32_t* __restrict__ cu,
                                                               int32_t* __restrict__ stats) {
@@ -167,90 +217,120 @@ __global__ __launch_bounds__(kDecideThreads) void plan_decide(PlanWs w, uint32_t
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int R = w.R, E = w.E, B = w.B, G = w.G, C = w.C;
     const int ncu = E + B + 1;
-    if (tid == 0) {
-        sh.status = 0; sh.nent = 0; sh.nd = 0; sh.nr = 0; sh.nred = 0;
-        sh.migr = 0; sh.nslot = 0; sh.nfb = 0; sh.fbrows = 0; sh.maxl = 0;
-    }
-    if (tid < R) sh.rank_n[tid] = 0;
-    __syncthreads();
-    int st = 0;
-    for (int i = tid; i < w.NCH; i += NT) st |= w.chunk_status[i];
-    if (st) atomicOr(&sh.status, st);
-    int ml = 0;
-    for (int e = tid; e < E; e += NT) {
-        const int l = w.L[e];
-        sh.L[e] = l;
-        sh.avail[e] = l;
-        sh.ecnt[e] = 0;
-        ml = max(ml, l);
-    }
-    atomicMax(&sh.maxl, ml);
-    __syncthreads();
-
-    // rank loads P[q] = rows wanting q's home group, X[q] = P[q] - C
-    if (tid < R) {
-        int p = 0;
-        for (int i = 0; i < G; ++i) p += sh.L[tid * G + i];
-        sh.P[tid] = p;
-        sh.X[tid] = p - C;
-    }
-    __syncthreads();
-
-    // donors by excess desc, receivers by deficit desc, ties to the lower rank: each rank
-    // counts the ranks of its kind ahead of it
-    if (tid < R && !(sh.status & kBad)) {
-        const int x = sh.X[tid];
-        if (x != 0) {
-            int pos = 0;
-            for (int q = 0; q < R; ++q) {
-                const int y = sh.X[q];
-                if (y != 0 && (x > 0) == (y > 0)) pos += (x > 0 ? y > x : y < x) || (y == x && q < tid);
+    // expert loads L[e] = sum of the segment totals.  With E <= 512 the segments of an expert are
+    // split over 512/E threads (strided), whose partial sums meet in LDS; the loads are only summed
+    // here, so they are in flight together (the segment offsets are stored during the chain).
+    int st = tid < w.NSEG ? w.chunk_status[tid] : 0;   // (more segments: below)
+    const int P = E <= NT ? min(NT / E, 8) : 1;
+    if (E <= NT) {
+        const int e = tid % E, part = tid / E;
+        if (part < P) {
+            int l = 0;
+            for (int s0 = part; s0 < w.NSEG; s0 += 16 * P) {
+                int v[16];
+#pragma unroll
+                for (int b = 0; b < 16; ++b) v[b] = w.segtot[(size_t)min(s0 + b * P, w.NSEG - 1) * E + e];
+#pragma unroll
+                for (int b = 0; b < 16; ++b) l += s0 + b * P < w.NSEG ? v[b] : 0;
             }
-            if (x > 0) {
-                sh.don[pos] = tid;
-                atomicAdd(&sh.nd, 1);
-            } else {
-                sh.rec[pos] = tid;
-                atomicAdd(&sh.nr, 1);
-            }
+            sh.lpart[tid] = l;
+        }
+    } else {
+        for (int e = tid; e < E; e += NT) {
+            int l = 0;
+#pragma unroll 16
+            for (int sg = 0; sg < w.NSEG; ++sg) l += w.segtot[(size_t)sg * E + e];
+            sh.L[e] = l;
         }
     }
-    __syncthreads();
+    for (int i = tid + NT; i < w.NSEG; i += NT) st |= w.chunk_status[i];
+    if (tid == 0) {
+        sh.status = 0;
+        sh.nent = 0;
+    }
+    if (tid < R) sh.rank_n[tid] = 0;
+    lds_sync();
+    if (st) atomicOr(&sh.status, st);
+    for (int e = tid; e < E; e += NT) {
+        int l = 0;
+        if (E <= NT) {
+            for (int p = 0; p < P; ++p) l += sh.lpart[p * E + e];
+            sh.L[e] = l;
+        } else {
+            l = sh.L[e];
+        }
+        sh.avail[e] = l;
+        sh.ecnt[e] = 0;
+    }
+    lds_sync();
+
+    // rank loads P[q] = rows wanting q's home group, X[q] = P[q] - C (one wave per rank, G <= 64)
+    for (int q = wave; q < R; q += NW) {
+        const int p = wave_sum(lane < G ? sh.L[q * G + lane] : 0);
+        if (lane == 0) {
+            sh.P[q] = p;
+            sh.X[q] = p - C;
+        }
+    }
+    lds_sync();
 
     // the duplicate chain, on wave 0; lane i holds the remaining rows of the donor's expert i
     if (wave == 0 && !(sh.status & kBad)) {
+        // donors by excess desc, receivers by deficit desc, ties to the lower rank: lane q counts
+        // the ranks of its kind ahead of it and writes its rank id there; the lanes then read each
+        // other's entries, after a wave barrier (a data exchange between lanes through LDS)
+        const int xq = lane < R ? sh.X[lane] : 0;
+        {
+            int pos = 0;
+            for (int q = 0; q < R; ++q) {
+                const int y = __builtin_amdgcn_readlane(xq, q);
+                pos += xq > 0 ? (y > xq || (y == xq && q < lane)) : (y < xq || (y == xq && q < lane));
+            }
+            if (xq > 0) sh.don[pos] = lane;
+            else if (xq < 0) sh.rec[pos] = lane;
+        }
+        wave_lds_sync();
         int fail = 0;
         int nent = 0;
+        // The donor group d being shipped from: lane i holds expert d*G+i's remaining rows (av),
+        // load (lv) and packed replica counters (cnt).  Every ship call of one donor iteration
+        // ships from that donor, so the group stays in registers for the whole iteration.
+        int av = 0, lv = 0, cnt = 0;
+        auto take_group = [&](int d) {
+            const int e = d * G + lane;
+            av = lane < G ? sh.avail[e] : 0;
+            lv = lane < G ? sh.L[e] : 0;
+            cnt = lane < G ? sh.ecnt[e] : 0;
+        };
+        auto put_group = [&](int d) {
+            if (lane < G) {
+                sh.avail[d * G + lane] = av;
+                sh.ecnt[d * G + lane] = cnt;
+            }
+        };
         // ship(d, t, amt): amt rows of donor group d's experts to rank t, best fit first.  Every
         // rank receives from one ship call only, so the entries this call makes on t are t's
-        // entries j = 0, 1, ... in creation order.  Lane i holds expert d*G+i while picking;
-        // the call's entry j is kept in lane j's registers and all are written after the call.
+        // entries j = 0, 1, ... in creation order; entry j is kept in lane j's registers and all
+        // are written after the call.
         auto ship = [&](int d, int t, int amt) {
-            const int e = d * G + lane;
-            int av = lane < G ? sh.avail[e] : 0;
-            const int lv = lane < G ? sh.L[e] : 0;
-            int cnt = lane < G ? sh.ecnt[e] : 0;
             int j = 0;
             int my_e = 0, my_a = 0, my_pre = 0, my_k = 0;
             while (amt > 0 && !fail) {
-                // best fit: fewest remaining rows that still cover amt (ties: lower id)
-                const bool cover = lane < G && av >= amt;
-                int m, pick;
-                if (__ballot(cover)) {
-                    m = wave_reduce<false>(cover ? av : INT_MAX);
-                    pick = first_lane(cover && av == m);
-                } else {
-                    // otherwise the most remaining rows (ties: lower id), all of them
-                    m = wave_reduce<true>(lane < G ? av : -1);
-                    pick = first_lane(lane < G && av == m);
-                }
-                const int a = m < amt ? m : amt;
+                // One unsigned minimum picks both ways: an expert that covers amt keys by its
+                // rows (best fit: fewest rows, ties to the lower id); one that does not keys above
+                // every covering key, by amt-1-av (most rows first, ties to the lower id).
+                const unsigned key = lane >= G ? 0xFFFFFFFFu
+                                     : av >= amt ? (unsigned)av
+                                                 : 0x80000000u | (unsigned)(amt - 1 - av);
+                const unsigned m = wave_reduce_u32(key);
+                const int pick = first_lane(key == m);
+                const int got = (m & 0x80000000u) ? amt - 1 - (int)(m & 0x7FFFFFFFu) : (int)m;
+                const int a = got < amt ? got : amt;
                 if (a <= 0 || nent + j >= E || j >= kMaxG) {
                     fail = a <= 0 ? MOONEP_ST_CAPACITY : MOONEP_ST_OVERFLOW;
                     break;
                 }
-                // the picked expert's counters and the rows it gave earlier replicas (read with
-                // every lane active)
+                // the picked expert's counters and the rows it gave earlier replicas
                 const int pc = __builtin_amdgcn_readlane(cnt, pick);
                 const int pre = __builtin_amdgcn_readlane(lv - av, pick);
                 const bool slot = j < B;
@@ -268,10 +348,6 @@ __global__ __launch_bounds__(kDecideThreads) void plan_decide(PlanWs w, uint32_t
                 ++j;
                 amt -= a;
             }
-            if (lane < G) {
-                sh.avail[e] = av;
-                sh.ecnt[e] = cnt;
-            }
             if (lane < j) {
                 const int i = nent + lane;
                 sh.ent_e[i] = my_e;
@@ -287,7 +363,7 @@ __global__ __launch_bounds__(kDecideThreads) void plan_decide(PlanWs w, uint32_t
             if (lane == 0) sh.rank_n[t] = j;
             nent += j;
         };
-        const int nd = sh.nd, nr = sh.nr;
+        const int nd = __popcll(__ballot(xq > 0)), nr = __popcll(__ballot(xq < 0));
         // lane r holds donor r and receiver r (in order) with their excess / deficit
         const int l_don = lane < nd ? sh.don[lane] : 0, l_rec = lane < nr ? sh.rec[lane] : 0;
         const int l_dx = lane < nd ? sh.X[l_don] : 0, l_rd = lane < nr ? -sh.X[l_rec] : 0;
@@ -299,6 +375,7 @@ __global__ __launch_bounds__(kDecideThreads) void plan_decide(PlanWs w, uint32_t
             for (int di = 0; di < nd && !fail; ++di) {
                 const int d = __builtin_amdgcn_readlane(l_don, di);
                 int rem = __builtin_amdgcn_readlane(l_dx, di);
+                take_group(d);
                 if (carry_t >= 0) {
                     ship(d, carry_t, carry_s);
                     rem -= carry_s;
@@ -311,6 +388,7 @@ __global__ __launch_bounds__(kDecideThreads) void plan_decide(PlanWs w, uint32_t
                     rem -= need;
                     ++jr;
                 }
+                put_group(d);
                 if (rem < 0) {
                     carry_t = d;
                     carry_s = -rem;
@@ -332,6 +410,7 @@ __global__ __launch_bounds__(kDecideThreads) void plan_decide(PlanWs w, uint32_t
                 int rem = __builtin_amdgcn_readlane(l_dx, di) + handed;
                 const bool may_repay = handed == 0;
                 handed = 0;
+                take_group(d);
                 if (carry_t >= 0) {
                     ship(d, carry_t, carry_s);
                     rem -= carry_s;
@@ -370,6 +449,7 @@ __global__ __launch_bounds__(kDecideThreads) void plan_decide(PlanWs w, uint32_t
                     rem -= need;
                     if (lane == r) left = false;
                 }
+                put_group(d);
                 if (rem < 0) {
                     carry_t = d;
                     carry_s = -rem;
@@ -383,8 +463,29 @@ __global__ __launch_bounds__(kDecideThreads) void plan_decide(PlanWs w, uint32_t
             sh.nent = fail ? 0 : nent;
             if (fail) sh.status |= fail;
         }
+    } else if (wave % 4 != 0) {
+        // meanwhile, on the waves that do not share wave 0's SIMD: each segment's offset per
+        // expert (pairs of e in the earlier segments), for plan_dest; 32 segments' totals are
+        // loaded before their offsets are stored
+        constexpr int kHelpers = NT - NT / 4;
+        const int hid = (wave - 1 - wave / 4) * 64 + lane;
+        for (int e = hid; e < E; e += kHelpers) {
+            int l = 0;
+            for (int s0 = 0; s0 < w.NSEG; s0 += 32) {
+                // unconditional loads (segments past the end re-read the last one), all in flight
+                int v[32];
+#pragma unroll
+                for (int b = 0; b < 32; ++b) v[b] = w.segtot[(size_t)min(s0 + b, w.NSEG - 1) * E + e];
+                const int nb = min(32, w.NSEG - s0);
+#pragma unroll
+                for (int b = 0; b < 32; ++b) {
+                    if (b < nb) w.segpre[(size_t)(s0 + b) * E + e] = l;
+                    l += b < nb ? v[b] : 0;
+                }
+            }
+        }
     }
-    __syncthreads();
+    lds_sync();
 
     // rows kept by each home group before each expert, and how many of those experts keep rows
     // (wave-wide scans per rank; G <= 64)
@@ -411,7 +512,7 @@ __global__ __launch_bounds__(kDecideThreads) void plan_decide(PlanWs w, uint32_t
             sh.nzbase[q + 1] = c;
         }
     }
-    __syncthreads();
+    lds_sync();
     // non-empty home groups before each rank (R <= 64: one wave)
     if (wave == 0) {
         const int v = lane < R ? sh.nzbase[lane + 1] : 0;
@@ -427,7 +528,7 @@ __global__ __launch_bounds__(kDecideThreads) void plan_decide(PlanWs w, uint32_t
     // every rank must total exactly S*K rows [TC, text under Table 1]
     if (tid < R && !(sh.status & kBad) && cu_at(sh, tid, E + B, E, G, B) != C)
         atomicOr(&sh.status, MOONEP_ST_CAPACITY);
-    __syncthreads();
+    lds_sync();
     const bool ok = (sh.status & kBad) == 0;
     const int nent = ok ? sh.nent : 0;
 
@@ -448,7 +549,6 @@ __global__ __launch_bounds__(kDecideThreads) void plan_decide(PlanWs w, uint32_t
             n = 1 + (c & 0x3FF);
             nred = (c >> 10) & 0x3FF;
             nfb = (c >> 20) & 0x3FF;
-            if (nred > 0) atomicAdd(&sh.nred, 1);
             // GEMM groups: non-empty home groups in expert order, then the entries'
             if (av > 0) w.groups[sh.nzbase[h] + sh.nzpre[e]] = Group{hs.row0, av, e, e};
         }
@@ -473,11 +573,10 @@ __global__ __launch_bounds__(kDecideThreads) void plan_decide(PlanWs w, uint32_t
     }
     // zero row segment read by masked GEMM tile loads
     for (int i = tid; i < kZeroElems / 2; i += NT) reinterpret_cast<uint32_t*>(w.zeros)[i] = 0u;
-    __syncthreads();
+    lds_sync();
 
     // per entry: its instance, reduce slot or fallback segment, GEMM group
     const int nhome = sh.nzbase[R];
-    int migr = 0, nslot = 0, nfb = 0, fbrows = 0;
     for (int i = tid; i < nent; i += NT) {
         const int e = sh.ent_e[i], q = sh.ent_q[i], a = sh.ent_a[i], jj = sh.ent_j[i];
         const int k = sh.ent_k[i] & 0xFFFF, kk = sh.ent_k[i] >> 16;
@@ -490,13 +589,9 @@ __global__ __launch_bounds__(kDecideThreads) void plan_decide(PlanWs w, uint32_t
         in[2] = row0 - stt;
         if (wr >= E) {
             w.red_slot[(size_t)e * kMaxR + kk] = q * B + jj;
-            ++nslot;
         } else {
             w.fb_seg[(size_t)e * kMaxR + kk] = Segment{row0, a};
-            ++nfb;
-            fbrows += a;
         }
-        migr += a;
         int32_t* en = w.entries + (size_t)i * 5;
         en[0] = e;
         en[1] = q;
@@ -505,37 +600,59 @@ __global__ __launch_bounds__(kDecideThreads) void plan_decide(PlanWs w, uint32_t
         en[4] = wr;
         w.groups[nhome + i] = Group{row0, a, wr < E ? wr : -1 - (q * B + jj), e};
     }
-    if (migr) atomicAdd(&sh.migr, migr);
-    if (nslot) atomicAdd(&sh.nslot, nslot);
-    if (nfb) atomicAdd(&sh.nfb, nfb);
-    if (fbrows) atomicAdd(&sh.fbrows, fbrows);
-    // cu_seqlens: rows of rank q whose weight row is below p, every (q, p) at once
-    for (int i = tid; i < R * ncu; i += NT) {
-        const int q = i / ncu, p = i % ncu;
-        cu[i] = ok ? cu_at(sh, q, p, E, G, B) : 0;
-    }
-    __syncthreads();
-
-    if (tid == 0) {
-        int maxper = 0, bound = 0, maxp = 0, minp = 0x7fffffff, nd = 0, nr = 0;
-        for (int q = 0; q < R; ++q) {
-            if (ok) maxper = max(maxper, sh.rank_n[q]);
-            bound += sh.X[q] > 0 ? sh.X[q] : 0;
-            maxp = max(maxp, sh.P[q]);
-            minp = min(minp, sh.P[q]);
-            nd += sh.X[q] > 0;
-            nr += sh.X[q] < 0;
+    // cu_seqlens: rows of rank q whose weight row is below p; one wave per rank, lanes over p, the
+    // rank's few replicas (weight row, rows) taken from lanes of a register
+    for (int q = wave; q < R; q += NW) {
+        const int n = ok ? sh.rank_n[q] : 0;
+        const int lw = lane < n ? sh.rank_w[q][lane] : 0, la = lane < n ? sh.rank_a[q][lane] : 0;
+        const int h0 = q * G, ht = sh.hometot[q];
+        for (int p = lane; p < ncu; p += 64) {
+            int c = p <= h0 ? 0 : p >= h0 + G ? ht : sh.homepre[p];
+            for (int j = 0; j < n; ++j)
+                c += __builtin_amdgcn_readlane(lw, j) < p ? __builtin_amdgcn_readlane(la, j) : 0;
+            cu[(size_t)q * ncu + p] = ok ? c : 0;
         }
+    }
+    lds_sync();
+
+    // statistics, on wave 0: sums over the entries, the experts and the ranks
+    if (wave == 0) {
+        int migr = 0, nsf = 0, fbrows = 0, nred = 0, maxl = 0;
+        for (int i = lane; i < nent; i += 64) {
+            const int a = sh.ent_a[i];
+            const bool slot = sh.ent_j[i] < B;
+            migr += a;
+            nsf += slot ? 1 : 1 << 16;       // slot replicas | fallback replicas << 16
+            fbrows += slot ? 0 : a;
+        }
+        for (int e = lane; e < E; e += 64) {
+            nred += ok && ((sh.ecnt[e] >> 10) & 0x3FF) > 0;
+            maxl = max(maxl, sh.L[e]);
+        }
+        const int x = lane < R ? sh.X[lane] : 0, pr = lane < R ? sh.P[lane] : 0;
+        migr = wave_sum(migr);
+        nsf = wave_sum(nsf);
+        fbrows = wave_sum(fbrows);
+        nred = wave_sum(nred);
+        maxl = wave_reduce<true>(maxl);
+        const int bound = wave_sum(x > 0 ? x : 0);
+        const int maxp = wave_reduce<true>(lane < R ? pr : INT_MIN);
+        const int minp = wave_reduce<false>(lane < R ? pr : INT_MAX);
+        const int maxper = ok ? wave_reduce<true>(lane < R ? sh.rank_n[lane] : 0) : 0;
+        const int nd = __popcll(__ballot(x > 0)), nr = __popcll(__ballot(x < 0));
+        const int nslot = nsf & 0xFFFF, nfb = nsf >> 16;
         int status = sh.status;
-        if (ok && sh.nfb > 0 && (flags & MOONEP_TRAINING)) status |= MOONEP_ST_TRAIN_FALLBACK;
-        const int v[MOONEP_NSTATS] = {status, nent, sh.nslot, sh.nfb, sh.fbrows, sh.migr, bound, sh.maxl,
-                                      maxp, minp, nd, nr, maxper, ok ? R * C : 0, 0, 0};
-        for (int i = 0; i < MOONEP_NSTATS; ++i) stats[i] = v[i];
-        w.hdr[HDR_STATUS] = status;
-        w.hdr[HDR_NENTRIES] = nent;
-        w.hdr[HDR_NGROUPS] = ok ? nhome + nent : 0;
-        w.hdr[HDR_NSLOTREP] = sh.nslot;
-        w.hdr[HDR_NRED] = ok ? sh.nred : 0;
+        if (ok && nfb > 0 && (flags & MOONEP_TRAINING)) status |= MOONEP_ST_TRAIN_FALLBACK;
+        if (lane == 0) {
+            const int v[MOONEP_NSTATS] = {status, nent, nslot, nfb, fbrows, migr, bound, maxl,
+                                          maxp, minp, nd, nr, maxper, ok ? R * C : 0, 0, 0};
+            for (int i = 0; i < MOONEP_NSTATS; ++i) stats[i] = v[i];
+            w.hdr[HDR_STATUS] = status;
+            w.hdr[HDR_NENTRIES] = nent;
+            w.hdr[HDR_NGROUPS] = ok ? nhome + nent : 0;
+            w.hdr[HDR_NSLOTREP] = nslot;
+            w.hdr[HDR_NRED] = ok ? nred : 0;
+        }
     }
 }
 
@@ -546,7 +663,7 @@ constexpr int kDestBatch = 8;
 __global__ __launch_bounds__(64) void plan_dest(const int32_t* __restrict__ topk, PlanWs w,
                                                 int32_t* __restrict__ dest) {
     const int ch = blockIdx.x;
-    const int r = ch / w.NC, c = ch % w.NC;
+    const int r = ch / w.NC, c = ch % w.NC, seg = ch / w.SEG;
     const int t = threadIdx.x;
     const int s = c * kChunk + t;
     if (s >= w.S) return;
@@ -568,7 +685,9 @@ __global__ __launch_bounds__(64) void plan_dest(const int32_t* __restrict__ topk
             const bool v = !bad && (unsigned)e[b] < (unsigned)w.E;
             const int ee = v ? e[b] : 0;
             const int32_t* in = w.inst + (size_t)ee * kMaxR * 3;
-            g[b] = v ? w.cnt[(size_t)ee * w.NCH + ch] + __popcll(w.bm[(size_t)ch * w.E + ee] & low) : -1;
+            g[b] = v ? w.segpre[(size_t)seg * w.E + ee] + w.cnt[(size_t)ch * w.E + ee] +
+                           __popcll(w.bm[(size_t)ch * w.E + ee] & low)
+                     : -1;
             ni[b] = v ? min(w.ninst[ee], kMaxR) : 0;
             i01[b] = v ? *reinterpret_cast<const int4*>(in) : make_int4(0, 0, 0, 0);
             i2[b] = v ? *reinterpret_cast<const int2*>(in + 4) : make_int2(0, 0);
@@ -618,9 +737,7 @@ static int launch_plan(const moonep_dims_t* dims, const int32_t* topk, void* pla
     PlanWs w;
     plan_ws_layout(dims, plan_ws, &w);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipLaunchKernelGGL(plan_hist, dim3(w.NCH), dim3(64), (size_t)w.E * 8, s, topk, w);
-    MOONEP_LAUNCH_CHECK();
-    hipLaunchKernelGGL(plan_scan, dim3((w.E + 3) / 4), dim3(256), 0, s, w);
+    hipLaunchKernelGGL(plan_hist, dim3(w.NSEG), dim3(kHistThreads), (size_t)w.SEG * w.E * 8, s, topk, w);
     MOONEP_LAUNCH_CHECK();
     static const bool decide_smem_ok =
         hipFuncSetAttribute(reinterpret_cast<const void*>(plan_decide), hipFuncAttributeMaxDynamicSharedMemorySize,
