@@ -21,7 +21,7 @@ constexpr int kMaxK = 16;
 // chunks per planning histogram segment, at most (fewer segments: less for plan_decide to sum;
 // more: more workgroups for plan_hist)
 #ifndef MOONEP_PLAN_SEG
-#define MOONEP_PLAN_SEG 16
+#define MOONEP_PLAN_SEG 8
 #endif
 constexpr int kSegMax = MOONEP_PLAN_SEG;
 constexpr int kZeroElems = 512;      // zero bf16 elements kept in the plan workspace

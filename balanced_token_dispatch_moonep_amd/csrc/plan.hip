@@ -9,7 +9,7 @@
 // rank serves exactly C = S*K rows [TC, "What the technique is" and its flowchart;
 // TD, summary; AL, How it works].  Three launches:
 //
-//   plan_hist   one workgroup per segment of up to 16 consecutive 64-token chunks (one wave
+//   plan_hist   one workgroup per segment of up to 8 consecutive 64-token chunks (one wave
 //               per chunk, topk loads issued before the atomics): an LDS
 //               bitmap per chunk and expert (bit t = token t of the chunk picked the expert),
 //               built with LDS atomic OR (order-free, so the result is deterministic); per
@@ -39,12 +39,12 @@ namespace moonep {
 constexpr int kBad = MOONEP_ST_BAD_ID | MOONEP_ST_DUP_ID | MOONEP_ST_CAPACITY | MOONEP_ST_OVERFLOW;
 
 // One workgroup per segment of SEG consecutive chunks (in (rank, token) order), one wave per
-// chunk (a wave takes chunks wave and wave + 16 of a 32-chunk segment, its topk loads for both
-// issued before either chunk's atomics): LDS bitmaps per chunk and expert (bit t = token t of the
-// chunk picked the expert), built with LDS atomic OR (order-free, so the result is
-// deterministic).  Then, per expert, the exclusive prefix of the popcounts over the segment's
-// chunks and the segment total.  A bit already set flags a duplicate expert within a token.
-constexpr int kHistThreads = 1024, kHistWaves = kHistThreads / 64;
+// chunk (with more chunks than waves a wave takes several, its topk loads for all of them issued
+// before any chunk's atomics): LDS bitmaps per chunk and expert (bit t = token t of the chunk
+// picked the expert), built with LDS atomic OR (order-free, so the result is deterministic).
+// Then, per expert, the exclusive prefix of the popcounts over the segment's chunks and the
+// segment total.  A bit already set flags a duplicate expert within a token.
+constexpr int kHistWaves = kSegMax < 16 ? kSegMax : 16, kHistThreads = 64 * kHistWaves;
 constexpr int kHistRounds = (kSegMax + kHistWaves - 1) / kHistWaves;
 __global__ __launch_bounds__(kHistThreads) void plan_hist(const int32_t* __restrict__ topk, PlanWs w) {
     extern __shared__ unsigned long long sbm[];   // [SEG][E]
@@ -226,12 +226,12 @@ __global__ __launch_bounds__(kDecideThreads) void plan_decide(PlanWs w, uint32_t
         const int e = tid % E, part = tid / E;
         if (part < P) {
             int l = 0;
-            for (int s0 = part; s0 < w.NSEG; s0 += 16 * P) {
-                int v[16];
+            for (int s0 = part; s0 < w.NSEG; s0 += 32 * P) {
+                int v[32];
 #pragma unroll
-                for (int b = 0; b < 16; ++b) v[b] = w.segtot[(size_t)min(s0 + b * P, w.NSEG - 1) * E + e];
+                for (int b = 0; b < 32; ++b) v[b] = w.segtot[(size_t)min(s0 + b * P, w.NSEG - 1) * E + e];
 #pragma unroll
-                for (int b = 0; b < 16; ++b) l += s0 + b * P < w.NSEG ? v[b] : 0;
+                for (int b = 0; b < 32; ++b) l += s0 + b * P < w.NSEG ? v[b] : 0;
             }
             sh.lpart[tid] = l;
         }

@@ -140,7 +140,7 @@ int moonep_plan(const moonep_dims_t* dims, const int32_t* topk, void* plan_ws,
  *   topk, cu_seqlens, dest, stats  as for moonep_plan
  * Returns MOONEP_ETOOBIG (nothing enqueued) when moonep_plan_workspace_bytes(dims) exceeds
  * MOONEP_NOALLOC_WS_BYTES (8 MiB: e.g. R=8, E=256, S=4096, K=8 needs 2.1 MB; R=8, E=384,
- * S=8192, K=8 about 5.5 MB), MOONEP_EHIP if the array's device address cannot be obtained.
+ * S=8192, K=8 about 5.7 MB), MOONEP_EHIP if the array's device address cannot be obtained.
  * Every call on one GPU uses that GPU's one array: calls that overlap on a GPU (other streams,
  * other host threads) race and must be serialised by the caller. */
 #define MOONEP_NOALLOC_WS_BYTES (8u << 20)
