@@ -92,6 +92,10 @@ def test_plan_degenerate_routings(kind, B, training, rule):
     # 64 home experts per rank, the most a rank's group may hold (one lane per expert in the
     # planner's replica chain)
     (2, 128, 128, 8, 4, 1.0), (8, 512, 96, 8, 4, 0.8), (4, 256, 64, 8, 0, 1.5),
+    # 4,160 chunks (a ragged last one per rank): more than 512 histogram segments, so the
+    # decision kernel's threads each read several segment status words and sum their experts'
+    # segment totals in several batches
+    (64, 128, 4150, 2, 2, 1.0),
 ])
 @pytest.mark.parametrize("rule", RULES)
 def test_plan_shapes(R, E, S, K, B, lam, rule):
