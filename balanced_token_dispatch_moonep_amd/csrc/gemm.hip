@@ -31,8 +31,11 @@
 //   * Persistent grid (one workgroup per CU).  Row kernels: tiles are ordered group-major,
 //     then n-tile, then m-tile, and each XCD (blockIdx % 8) takes a contiguous range of them,
 //     handed out in order from a per-XCD counter, so tiles sharing a weight or activation
-//     panel run on the same XCD together; rows and columns outside a tile clamp to the last
-//     valid one.  Weight-gradient kernel: tiles are
+//     panel run on the same XCD together.  Activation rows past a group's end (row-tile
+//     padding, 12% of the rows here) load zeros through the range check of a buffer resource,
+//     so their MFMAs run on zero operands, which draw less power (measured: the row kernels
+//     ran 1-4% faster than with copies of the last valid row); weight columns outside a tile
+//     clamp to the last valid one.  Weight-gradient kernel: tiles are
 //     handed out dynamically, largest target first, and the loop is software-pipelined by one
 //     tile (the next tile's first copies go out before this tile's stores); rows past a
 //     segment's end load from a zero block kept in the plan workspace.
@@ -145,6 +148,24 @@ __device__ __forceinline__ void dma16(const uint16_t* g, uint32_t lds) {
 __device__ __forceinline__ void dma16s(const uint16_t* base, uint32_t voff, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds)
                  : "memory", "m0");
+}
+// The same copy through a buffer resource (base and byte limit in four scalar registers): a lane
+// whose offset lies past the limit gets zeros (the range check of buffer loads).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void dma16b(u32x4_t rsrc, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "s"(lds)
+                 : "memory", "m0");
+}
+// Raw buffer resource over [base, base + 0xFFFFFFF0): offsets of padding rows are set to the limit.
+constexpr uint32_t kZeroOff = 0xFFFFFFF0u;
+__device__ __forceinline__ u32x4_t rsrc_of(const void* base) {
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    u32x4_t r;
+    r.x = __builtin_amdgcn_readfirstlane((uint32_t)p);
+    r.y = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32) & 0xFFFFu);
+    r.z = kZeroOff;
+    r.w = 0x00020000u;   // 32-bit data format, no swizzle, no stride
+    return r;
 }
 #pragma clang diagnostic pop
 // Next ticket of a tile counter.  An atomic increment rather than an add: the compiler rewrites
@@ -781,16 +802,17 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_rows_kernel(GemmArgs a) {
                                          : a.Bslot + (size_t)(-1 - gr.wsel) * a.bstride;
 
         // per-lane sources of this wave's DMA loads (2*PARTS per operand and stage), as byte
-        // offsets from the stage's operand base; rows and columns outside the tile clamp to the
-        // last valid one (their products only reach outputs the epilogue does not store)
+        // offsets from the stage's operand base; activation rows past the group's end get an
+        // offset beyond the buffer resource's limit (zeros), weight columns outside the tile clamp
+        // to the last valid one (their products only reach outputs the epilogue does not store)
         constexpr int P2 = 2 * L::PARTS;
         uint32_t ao[P2], bo[P2];
 #pragma unroll
         for (int i = 0; i < P2; ++i) {
             const int p = (wave * P2 + i) * 64 + lane;
-            {   // A: k-contiguous activations [rows, K]
+            {   // A: k-contiguous activations [rows, K]; rows past the group's end read zeros
                 const int r = p >> 3, c = (p & 7) ^ ((r >> 1) & 7);
-                ao[i] = 2u * (uint32_t)((row0 + min(r, mvalid - 1)) * a.lda + c * 8);
+                ao[i] = r < mvalid ? 2u * (uint32_t)((row0 + r) * a.lda + c * 8) : kZeroOff;
             }
             if (MODE == ROWS_BK) {   // weights [N, K]
                 const int r = p >> 3, c = (p & 7) ^ ((r >> 1) & 7);
@@ -815,14 +837,15 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_rows_kernel(GemmArgs a) {
         pipeline64<MODE == ROWS_BK, EPI, WN, EPI == EPI_STORE>(acc, smem, a.K / BK2, wm, wn, lane,
                                              [&](int op, int s, int buf, int i) {
             const uint32_t l = lds_wave + buf * OP2_BYTES + i * 1024;
-            // scalar stage base + per-lane offset; the dX kernel (k-contiguous weights, plain
-            // store) measured 4% faster with per-lane 64-bit addresses, so it keeps them
-            if constexpr (MODE == ROWS_BK && EPI == EPI_STORE) {
-                if (op == 0) dma16(A0 + (ao[i] / 2 + s * BK2), l);
-                else dma16(W + (bo[i] / 2 + s * bstep), l);
+            // activations through a buffer resource per stage (zeros for padding rows); weights
+            // from a scalar stage base + per-lane offset, except in the dX kernel (k-contiguous
+            // weights, plain store), which measured faster with per-lane 64-bit addresses
+            if (op == 0) {
+                dma16b(rsrc_of(A0 + s * BK2), ao[i], l);
+            } else if constexpr (MODE == ROWS_BK && EPI == EPI_STORE) {
+                dma16(W + (bo[i] / 2 + s * bstep), l);
             } else {
-                if (op == 0) dma16s(A0 + s * BK2, ao[i], l);
-                else dma16s(W + (size_t)s * bstep, bo[i], l);
+                dma16s(W + (size_t)s * bstep, bo[i], l);
             }
         });
         // the next tile's ticket is read here, while no stores are in flight: vmcnt retires in

@@ -397,6 +397,21 @@ def main():
     del src_buf, dst_buf
     log("[bench] hbm context", hbm_context)
 
+    # ---- the vendor library's dense bf16 product on the gate/up shape (context only: 2.5 PFLOP/s
+    # stays the denominator).  Dense rows (no grouping, no padding): R*S tokens x H @ H x 2I.
+    mm_a = torch.randn((R * S, H), dtype=torch.bfloat16, device=dev)
+    mm_b = torch.randn((H, 2 * I), dtype=torch.bfloat16, device=dev)
+    mm_flop = 2.0 * R * S * H * 2 * I
+    mm_gflops = _rate(lambda: mm_a @ mm_b, mm_flop)   # GFLOP/s (the helper divides by 1e9)
+    mfma_context = {
+        "torch_bf16_matmul_TFLOPs": round(mm_gflops / 1e3, 1),
+        "shape": f"{R * S}x{H} @ {H}x{2 * I}",
+        "frac_of_peak": round(mm_gflops / 1e3 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "gemm_gate_up_vs_it": round(rooflines["gemm_gate_up"]["achieved"] / (mm_gflops / 1e3), 4),
+    }
+    del mm_a, mm_b
+    log("[bench] mfma context", mfma_context)
+
     # ---- CPU oracle baseline on a bounded sample of the same workload ----------------------
     cpu = None
     if not args.no_cpu:
@@ -432,6 +447,7 @@ def main():
         "lognormal_planner": lognormal,
         "prefetch_pool": pool,
         "hbm_context": hbm_context,
+        "mfma_context": mfma_context,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
