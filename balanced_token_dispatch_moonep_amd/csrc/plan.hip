@@ -180,13 +180,13 @@ struct DecideShared {
     int avail[kMaxE];             // rows not (yet) given to a replica; keep[] after the chain
     int ecnt[kMaxE];              // packed replica counters of each expert
     // plan entries (replicas) in creation order
-    int ent_e[kMaxE], ent_q[kMaxE], ent_a[kMaxE];
-    int ent_j[kMaxE];             // creation index among rank q's entries (slot E+j if j < B)
-    int ent_pre[kMaxE];           // rows of e given to earlier replicas of e
-    int ent_k[kMaxE];             // index among e's replicas | index among those of its kind << 16
-    int rank_ent[kMaxR][kMaxG];   // entry ids on each rank by creation index
-    int rank_w[kMaxR][kMaxG];     // their weight rows
-    int rank_a[kMaxR][kMaxG];     // their rows
+    // (e, q, a, j): expert, rank, rows, creation index among rank q's entries (slot E+j if j < B)
+    int4 ent[kMaxE];
+    // (pre, k): rows of e given to earlier replicas of e; index among e's replicas | index among
+    // those of its kind << 16
+    int2 ent2[kMaxE];
+    // the entries on each rank by creation index: (entry id, weight row, rows, expert)
+    int4 rank_e[kMaxR][kMaxG];
     int rank_n[kMaxR];            // entries on each rank
     int homepre[kMaxE];           // rows kept by the experts of e's home group before e
     int nzpre[kMaxE];             // experts of e's home group before e that keep rows
@@ -203,7 +203,10 @@ __device__ __forceinline__ int cu_at(const DecideShared& sh, int q, int w, int E
     const int h0 = q * G;
     int s = w <= h0 ? 0 : w >= h0 + G ? sh.hometot[q] : sh.homepre[w];
     const int n = sh.rank_n[q];
-    for (int j = 0; j < n; ++j) s += sh.rank_w[q][j] < w ? sh.rank_a[q][j] : 0;
+    for (int j = 0; j < n; ++j) {
+        const int4 r = sh.rank_e[q][j];
+        s += r.y < w ? r.z : 0;
+    }
     return s;
 }
 
@@ -335,30 +338,23 @@ __global__ __launch_bounds__(kDecideThreads) void plan_decide(PlanWs w, uint32_t
                 const int pre = __builtin_amdgcn_readlane(lv - av, pick);
                 const bool slot = j < B;
                 const int kind = slot ? (pc >> 10) & 0x3FF : (pc >> 20) & 0x3FF;
-                if (lane == j) {
-                    my_e = d * G + pick;
-                    my_a = a;
-                    my_pre = pre;
-                    my_k = (pc & 0x3FF) | (kind << 16);
-                }
-                if (lane == pick) {
-                    cnt += kCntAll + (slot ? kCntSlot : kCntFb);
-                    av -= a;
-                }
+                const int kcode = (pc & 0x3FF) | (kind << 16), ecode = d * G + pick;
+                const int inc = kCntAll + (slot ? kCntSlot : kCntFb);
+                const bool mine = lane == j, picked = lane == pick;
+                my_e = mine ? ecode : my_e;
+                my_a = mine ? a : my_a;
+                my_pre = mine ? pre : my_pre;
+                my_k = mine ? kcode : my_k;
+                cnt += picked ? inc : 0;
+                av -= picked ? a : 0;
                 ++j;
                 amt -= a;
             }
             if (lane < j) {
                 const int i = nent + lane;
-                sh.ent_e[i] = my_e;
-                sh.ent_q[i] = t;
-                sh.ent_a[i] = my_a;
-                sh.ent_j[i] = lane;
-                sh.ent_pre[i] = my_pre;
-                sh.ent_k[i] = my_k;
-                sh.rank_ent[t][lane] = i;
-                sh.rank_w[t][lane] = lane < B ? E + lane : my_e;
-                sh.rank_a[t][lane] = my_a;
+                sh.ent[i] = make_int4(my_e, t, my_a, lane);
+                sh.ent2[i] = make_int2(my_pre, my_k);
+                sh.rank_e[t][lane] = make_int4(i, lane < B ? E + lane : my_e, my_a, my_e);
             }
             if (lane == 0) sh.rank_n[t] = j;
             nent += j;
@@ -562,10 +558,10 @@ __global__ __launch_bounds__(kDecideThreads) void plan_decide(PlanWs w, uint32_t
         const int q = i / B, jj = i % B;
         int e = -1, row0 = 0, rows = 0;
         if (ok && jj < sh.rank_n[q]) {
-            const int ei = sh.rank_ent[q][jj];
-            e = sh.ent_e[ei];
+            const int4 r = sh.rank_e[q][jj];
+            e = r.w;
             row0 = q * C + cu_at(sh, q, E + jj, E, G, B);
-            rows = sh.ent_a[ei];
+            rows = r.z;
         }
         w.slot_e[i] = e;
         w.slot_row0[i] = row0;
@@ -578,11 +574,13 @@ __global__ __launch_bounds__(kDecideThreads) void plan_decide(PlanWs w, uint32_t
     // per entry: its instance, reduce slot or fallback segment, GEMM group
     const int nhome = sh.nzbase[R];
     for (int i = tid; i < nent; i += NT) {
-        const int e = sh.ent_e[i], q = sh.ent_q[i], a = sh.ent_a[i], jj = sh.ent_j[i];
-        const int k = sh.ent_k[i] & 0xFFFF, kk = sh.ent_k[i] >> 16;
+        const int4 en4 = sh.ent[i];
+        const int2 en2 = sh.ent2[i];
+        const int e = en4.x, q = en4.y, a = en4.z, jj = en4.w;
+        const int k = en2.y & 0xFFFF, kk = en2.y >> 16;
         const int wr = jj < B ? E + jj : e;
         const int row0 = q * C + cu_at(sh, q, wr, E, G, B);
-        const int stt = sh.avail[e] + sh.ent_pre[i];      // home rows first, then replicas in order
+        const int stt = sh.avail[e] + en2.x;      // home rows first, then replicas in order
         int32_t* in = w.inst + ((size_t)e * kMaxR + 1 + k) * 3;
         in[0] = stt;
         in[1] = a;
@@ -604,7 +602,8 @@ __global__ __launch_bounds__(kDecideThreads) void plan_decide(PlanWs w, uint32_t
     // rank's few replicas (weight row, rows) taken from lanes of a register
     for (int q = wave; q < R; q += NW) {
         const int n = ok ? sh.rank_n[q] : 0;
-        const int lw = lane < n ? sh.rank_w[q][lane] : 0, la = lane < n ? sh.rank_a[q][lane] : 0;
+        const int4 rl = lane < n ? sh.rank_e[q][lane] : make_int4(0, 0, 0, 0);
+        const int lw = rl.y, la = rl.z;
         const int h0 = q * G, ht = sh.hometot[q];
         for (int p = lane; p < ncu; p += 64) {
             int c = p <= h0 ? 0 : p >= h0 + G ? ht : sh.homepre[p];
@@ -619,8 +618,9 @@ __global__ __launch_bounds__(kDecideThreads) void plan_decide(PlanWs w, uint32_t
     if (wave == 0) {
         int migr = 0, nsf = 0, fbrows = 0, nred = 0, maxl = 0;
         for (int i = lane; i < nent; i += 64) {
-            const int a = sh.ent_a[i];
-            const bool slot = sh.ent_j[i] < B;
+            const int4 en4 = sh.ent[i];
+            const int a = en4.z;
+            const bool slot = en4.w < B;
             migr += a;
             nsf += slot ? 1 : 1 << 16;       // slot replicas | fallback replicas << 16
             fbrows += slot ? 0 : a;
