@@ -156,7 +156,10 @@ __device__ __forceinline__ void dma16b(u32x4_t rsrc, uint32_t voff, uint32_t lds
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "s"(lds)
                  : "memory", "m0");
 }
-// Raw buffer resource over [base, base + 0xFFFFFFF0): offsets of padding rows are set to the limit.
+// Raw buffer resource over [base, base + 0xFFFFFFF0): offsets of padding rows are set to the limit,
+// and the range check (per dword, offset >= limit) returns zeros for them.  Every valid copy ends
+// below it: check_ffn_dims keeps rows * K below 2^31 elements with K a multiple of 64, so a
+// row's 16-byte chunks end at or below 2^32 - 128 bytes from the operand's start.
 constexpr uint32_t kZeroOff = 0xFFFFFFF0u;
 __device__ __forceinline__ u32x4_t rsrc_of(const void* base) {
     const uint64_t p = reinterpret_cast<uint64_t>(base);
