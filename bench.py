@@ -403,13 +403,25 @@ def main():
     mm_b = torch.randn((H, 2 * I), dtype=torch.bfloat16, device=dev)
     mm_flop = 2.0 * R * S * H * 2 * I
     mm_gflops = _rate(lambda: mm_a @ mm_b, mm_flop)   # GFLOP/s (the helper divides by 1e9)
+    del mm_a, mm_b
+    # ... and its batched product on the weight-gradient shape: per expert, H x (rows) @ (rows) x 2I
+    # with rows = one expert's mean share of the receive buffer and float32 output, as dW13 writes
+    # (64 experts' worth; operands contiguous)
+    nb_t, kr = 64, max(32, (R * S * K) // (E + R * B))
+    bm_a = torch.randn((nb_t, H, kr), dtype=torch.bfloat16, device=dev).contiguous()
+    bm_b = torch.randn((nb_t, kr, 2 * I), dtype=torch.bfloat16, device=dev).contiguous()
+    bm_gflops = _rate(lambda: torch.bmm(bm_a, bm_b, out_dtype=torch.float32), 2.0 * nb_t * H * kr * 2 * I)
+    del bm_a, bm_b
+    torch.cuda.empty_cache()
     mfma_context = {
         "torch_bf16_matmul_TFLOPs": round(mm_gflops / 1e3, 1),
         "shape": f"{R * S}x{H} @ {H}x{2 * I}",
         "frac_of_peak": round(mm_gflops / 1e3 / MFMA_BF16_PEAK_TFLOPS, 4),
         "gemm_gate_up_vs_it": round(rooflines["gemm_gate_up"]["achieved"] / (mm_gflops / 1e3), 4),
+        "torch_bf16_bmm_fp32_out_TFLOPs": round(bm_gflops / 1e3, 1),
+        "bmm_shape": f"{nb_t} x ({H}x{kr} @ {kr}x{2 * I}), float32 out",
+        "gemm_dw13_vs_it": round(rooflines["gemm_dw13"]["achieved"] / (bm_gflops / 1e3), 4),
     }
-    del mm_a, mm_b
     log("[bench] mfma context", mfma_context)
 
     # ---- CPU oracle baseline on a bounded sample of the same workload ----------------------
