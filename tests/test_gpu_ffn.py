@@ -101,6 +101,26 @@ def test_backward_mid(B):
     _backward_check(MID.with_(B=B))
 
 
+# H and I multiples of 512: the row GEMMs may compute the tails of at most 128 rows as 128 x 512
+# tiles (a second launch); the plan must hold such tails for the case to exercise them
+WIDE = MID.with_(H=512, I=512, S=400, seed=6)
+
+
+def _short_tails(cfg):
+    topk, _, _ = W.routing_for(cfg)
+    plan = O.make_plan(topk, cfg.E, cfg.B)
+    rows = np.diff(np.asarray(plan.cu), axis=1).ravel()
+    return int(np.sum((rows % 256 > 0) & (rows % 256 <= 128)))
+
+
+@pytest.mark.parametrize("B", [4, 0])
+def test_forward_backward_short_tails(B):
+    cfg = WIDE.with_(B=B)
+    assert _short_tails(cfg) >= 4
+    _forward_check(cfg)
+    _backward_check(cfg)
+
+
 def _random_cfgs(n=4, seed=11):
     """Seeded random small layers: rank counts, slots (including none, so fallback targets with
     several row segments), top-k, ragged H and I, and skew all vary."""
