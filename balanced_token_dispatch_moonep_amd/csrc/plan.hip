@@ -9,23 +9,22 @@
 // rank serves exactly C = S*K rows [TC, "What the technique is" and its flowchart;
 // TD, summary; AL, How it works].  Three launches:
 //
-//   plan_hist   one workgroup per segment of up to 8 consecutive 64-token chunks (one wave
-//               per chunk, topk loads issued before the atomics): an LDS
-//               bitmap per chunk and expert (bit t = token t of the chunk picked the expert),
-//               built with LDS atomic OR (order-free, so the result is deterministic); per
-//               expert, the exclusive prefix of the chunk popcounts within the segment and the
-//               segment total.  A bit already set flags a duplicate expert within a token.
+//   plan_hist   one workgroup per segment of up to 8 consecutive 64-token chunks, one wave per
+//               chunk (its topk loads issued before its atomics): an LDS bitmap per chunk and
+//               expert (bit t = token t of the chunk picked the expert), built with LDS atomic
+//               OR (order-free, so the result is deterministic); per expert, the exclusive
+//               prefix of the chunk popcounts within the segment and the segment total.  A bit
+//               already set flags a duplicate expert within a token.
 //   plan_decide one workgroup: expert loads L[e] (sums of the segment totals) and each
-//               segment's offset per expert, rank loads, donors/receivers, the duplicate chain with
-//               best-fit picks done as wave-wide argmin/argmax (at most one remote home
-//               group per rank [TC, Installation and integration]), prefetch slots or
-//               home-row fallback [TD, memory contract], cu_seqlens per rank and weight
-//               row, instance offsets, GEMM group tables, the weight-gradient work order
-//               (targets by rows, descending) and statistics.
+//               segment's offset per expert, rank loads, donors/receivers, the duplicate chain
+//               with best-fit picks done as wave-wide minima (at most one remote home group per
+//               rank [TC, Installation and integration]), prefetch slots or home-row fallback
+//               [TD, memory contract], cu_seqlens per rank and weight row, instance offsets,
+//               GEMM group tables and statistics.
 //   plan_dest   one wave per chunk: pair index g = segment offset + prefix within the segment
-//               + popcount of the lower bits of the expert's bitmap; the instance holding g gives the final row
-//               (the send side computes the receiver's position [TC, "What the technique
-//               is"]).
+//               + popcount of the lower bits of the expert's bitmap; the instance holding g
+//               gives the final row (the send side computes the receiver's position [TC, "What
+//               the technique is"]).
 //
 // Ties always go to the lower rank / expert id; integer arithmetic only, so the
 // result is bit-identical from run to run.
