@@ -96,8 +96,9 @@ struct GemmArgs {
     float* dw_home;           // EPI_ACC_F32: [E, M, N]
     float* dw_slot;           // EPI_ACC_F32: [R*B, M, N]
     int ntiles_n;
-    int* counter;             // tile counter(s), zero at launch (dW: one; row kernels: one per XCD)
+    int* counter;             // tile counters, one per XCD, zero at launch
     int accum;                // dW: add into the outputs (1) or write them (0)
+    int dw_fn, dw_bm, dw_bn;  // dW: XCD x takes the tile block (x / dw_fn, x % dw_fn) of dw_bm x dw_bn
 };
 
 // ---------------------------------------------------------------------------
@@ -877,7 +878,18 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_rows_kernel(GemmArgs a) {
 // Weight-gradient GEMM: dW[M, N] = A^T B (or += with MOONEP_GRAD_ACCUM) over the target's row
 // segments, where A = [rows, M] and B = [rows, N] are read m/n-contiguous.  Targets: t < E is
 // home expert t (its home rows plus its fallback replicas, in plan order), t >= E is prefetch
-// slot t - E.  Tiles are handed out dynamically, targets in descending row order.
+// slot t - E.  Targets are taken in descending row order.
+//
+// Tile order.  Each target's MT x NT tile grid is cut into eight blocks of dw_bm x dw_bn tiles
+// (the split with the fewest panels per block), one per XCD (workgroup b runs on XCD b mod 8).
+// The XCD's workgroups take its blocks, target after target, from the XCD's own counter, so
+// the tiles in flight on an XCD share dw_bm A panels and dw_bn B panels in its L2.  A tile
+// at position (i, j) of its block runs the full K steps of a one-segment target rotated by
+// 3(i + j) steps (its last, possibly partial, step stays last), so tiles that share a panel
+// read a slab some steps apart and the later reader can find it in L2 instead of waiting on
+// the same miss.  Against one global largest-first order this measured dW13 5.7% and dW2 4.4%
+// faster; a block without the rotation gained about 3.6% on dW13 and nothing on dW2, and
+// rotations of 1 to 5 steps per position measured within 1% of each other.
 // ---------------------------------------------------------------------------
 // WHICH (2 or 13) only separates the two weight-gradient launches' kernel names in traces.
 //
@@ -899,8 +911,12 @@ __global__ __launch_bounds__(DWT<TBN>::NTHR, TBN == 128 ? 2 : 1) void gemm_dw_ke
     const int wm = wave / T::WNN, wn = wave % T::WNN;
     const PlanWs& w = a.w;
     const int MT = (a.M + BM - 1) / BM, NT = a.ntiles_n;
-    const int per_target = MT * NT;
+    const int xcd = blockIdx.x % 8;
+    const int bm = a.dw_bm, bn = a.dw_bn;
+    const int bx = xcd / a.dw_fn, by = xcd % a.dw_fn;
+    const int per_target = bm * bn;                      // tiles of one target on this XCD
     const int total = (w.E + w.R * w.B) * per_target;
+    int* const counter = a.counter + xcd;
     float* ep = reinterpret_cast<float*>(smem + T::STG) + wave * 16 * T::EPL;
     // this wave's 1 KiB DMA slots of the A and B tiles of a stage
     const uint32_t lds_a = __builtin_amdgcn_readfirstlane(lds_addr(smem) + wave * T::PA * 1024);
@@ -917,20 +933,24 @@ __global__ __launch_bounds__(DWT<TBN>::NTHR, TBN == 128 ? 2 : 1) void gemm_dw_ke
         fs ^= 1;
         return r;
     };
-    auto fetch = [&]() {            // next tile id from the launch's counter
+    auto fetch = [&]() {            // next tile id from the XCD's counter
         int v = 0;
-        if (tid == 0) v = atomicAdd(a.counter, 1);
+        if (tid == 0) v = atomicAdd(counter, 1);
         return publish(v);
     };
-    // Descriptor of tile t; its row segments go to s_seg[par].  Returns false for a tile with
-    // nothing to do (an unused slot, or no rows in accumulate mode).  Target t < E is home expert
-    // t (its home rows, then its fallback replicas in plan order); t >= E is prefetch slot t - E.
-    int nseg = 0, nst = 0, m0 = 0, n0 = 0;
+    // Descriptor of this XCD's tile t; its row segments go to s_seg[par].  Returns false for a
+    // tile with nothing to do (past the grid's edge, an unused slot, or no rows in accumulate
+    // mode).  Target t < E is home expert t (its home rows, then its fallback replicas in plan
+    // order); t >= E is prefetch slot t - E.
+    int nseg = 0, nst = 0, m0 = 0, n0 = 0, rot = 0;
     float* out = nullptr;
     auto setup = [&](int t, int par) {
         const int target = w.dw_order[t / per_target];
         const int local = t % per_target;
-        const int nt = local / MT, mt = local % MT;
+        const int i = local % bm, j = local / bm;
+        const int mt = bx * bm + i, nt = by * bn + j;
+        if (mt >= MT || nt >= NT) return false;
+        rot = 3 * (i + j);
         if (target < w.E) {
             const Segment hs = w.home_seg[target];
             const int nfb = min(max(w.fb_n[target], 0), kMaxR - 1);
@@ -964,10 +984,16 @@ __global__ __launch_bounds__(DWT<TBN>::NTHR, TBN == 128 ? 2 : 1) void gemm_dw_ke
     // DMA issue state of the tile whose steps are being issued: per-lane byte offsets of each
     // load (k-row kk of the step, a 16-byte column chunk) from the step's first row, and a cursor
     // over the segments; columns outside the tile clamp to the last valid chunk (their products
-    // only reach outputs the epilogue does not store), rows past a segment's end load zeros
+    // only reach outputs the epilogue does not store), rows past a segment's end load zeros.
+    // The cursor counts rows in issue order (ikoff); a one-segment target's first rspan rows
+    // (its full steps before the last) are read rotated by roff rows: row phys(ikoff).
     uint32_t ao[T::PA], bo[T::PB];
-    int ipar = 0, iseg = 0, ikoff = 0;
+    int ipar = 0, iseg = 0, ikoff = 0, roff = 0, rspan = 0;
     Segment icur{0, 0};
+    auto phys = [&](int k) {
+        const int p = k + roff;
+        return k >= rspan ? k : (p >= rspan ? p - rspan : p);
+    };
     auto start_issue = [&](int par) {
 #pragma unroll
         for (int i = 0; i < T::PA; ++i) {
@@ -986,11 +1012,20 @@ __global__ __launch_bounds__(DWT<TBN>::NTHR, TBN == 128 ? 2 : 1) void gemm_dw_ke
         ikoff = 0;
         while (iseg < nseg && s_seg[par][iseg].rows <= 0) ++iseg;   // (never for a valid plan)
         icur = iseg < nseg ? s_seg[par][iseg] : Segment{0, 0};
+        roff = 0;
+        rspan = 0;
+        if (nseg == 1) {
+            const int full = (icur.rows - 1) / BK;   // steps before the last
+            if (full > 1) {
+                roff = (rot % full) * BK;
+                rspan = full * BK;
+            }
+        }
     };
     auto issue = [&](int, int buf, int i) {
         const uint32_t la = __builtin_amdgcn_readfirstlane(lds_a + buf * T::STAGE + i * 1024);
         const uint32_t lb = __builtin_amdgcn_readfirstlane(lds_b + buf * T::STAGE + i * 1024);
-        const int row = __builtin_amdgcn_readfirstlane(icur.row0 + ikoff);
+        const int row = __builtin_amdgcn_readfirstlane(icur.row0 + phys(ikoff));
         const int left = __builtin_amdgcn_readfirstlane(icur.rows - ikoff);
         const uint16_t* ga = a.A + (size_t)row * a.lda;
         const uint16_t* gb = a.B + (size_t)row * a.ldb;
@@ -1019,7 +1054,7 @@ __global__ __launch_bounds__(DWT<TBN>::NTHR, TBN == 128 ? 2 : 1) void gemm_dw_ke
     };
     // A full step that does not end its segment (more than BK rows left): no branches.
     auto issue_fast = [&](int, int buf, int i) {
-        const int row = __builtin_amdgcn_readfirstlane(icur.row0 + ikoff);
+        const int row = __builtin_amdgcn_readfirstlane(icur.row0 + phys(ikoff));
         dma16s(a.A + (size_t)row * a.lda, ao[i], __builtin_amdgcn_readfirstlane(lds_a + buf * T::STAGE + i * 1024));
         if (i < T::PB)
             dma16s(a.B + (size_t)row * a.ldb, bo[i], __builtin_amdgcn_readfirstlane(lds_b + buf * T::STAGE + i * 1024));
@@ -1039,7 +1074,7 @@ __global__ __launch_bounds__(DWT<TBN>::NTHR, TBN == 128 ? 2 : 1) void gemm_dw_ke
     }
     while (have) {
         int nxt = 0;
-        if (tid == 0) nxt = atomicAdd(a.counter, 1);   // consumed after the main loop (an atomic
+        if (tid == 0) nxt = atomicAdd(counter, 1);     // consumed after the main loop (an atomic
                                                        // add on purpose: see the loop's header)
         f32x16_t acc[4][2];
         zero_acc<2>(acc);
@@ -1078,7 +1113,7 @@ __global__ __launch_bounds__(kOrderThreads) void dw_prepare_kernel(PlanWs w, int
     extern __shared__ unsigned long long okey[];   // [E + R*B]
     const int tid = threadIdx.x;
     const int ntarget = w.E + w.R * w.B;
-    if (tid == 0) *counter = 0;
+    if (tid < 8) counter[tid] = 0;
     for (int t = tid; t < ntarget; t += kOrderThreads) {
         int rows = 0;
         if (t < w.E) {
@@ -1157,10 +1192,24 @@ static int launch_rows(int epi, int mode, const GemmArgs& a0, hipStream_t s) {
     return MOONEP_OK;
 }
 
-// Resets the launch's tile counter and orders the targets, then runs the dynamic-tile
-// weight-gradient kernel.
+// Resets the launch's eight per-XCD tile counters and orders the targets, then runs the
+// weight-gradient kernel with each target's tile grid cut into eight blocks (fm x 8/fm of them;
+// the split with the fewest panels per block, dw_bm + dw_bn).
 template <int WHICH>
-static int launch_dw(const GemmArgs& a, hipStream_t s) {
+static int launch_dw(const GemmArgs& a0, hipStream_t s) {
+    GemmArgs a = a0;
+    const int MT = (a.M + BM - 1) / BM, NT = a.ntiles_n;
+    a.dw_fn = 8;
+    a.dw_bm = MT;
+    a.dw_bn = (NT + 7) / 8;
+    for (int fm = 2; fm <= 8; fm *= 2) {
+        const int bm = (MT + fm - 1) / fm, bn = (NT + 8 / fm - 1) / (8 / fm);
+        if (bm + bn < a.dw_bm + a.dw_bn) {
+            a.dw_fn = 8 / fm;
+            a.dw_bm = bm;
+            a.dw_bn = bn;
+        }
+    }
     constexpr int smem = DWT<DW_TBN>::SMEM;
     static bool ok = set_smem(gemm_dw_kernel<DW_TBN, WHICH>, smem);
     if (!ok) return MOONEP_EHIP;
@@ -1335,7 +1384,7 @@ extern "C" int moonep_grouped_ffn_backward(const moonep_dims_t* dims, const void
     d.dw_home = dw2_home;
     d.dw_slot = dw2_red;
     d.ntiles_n = (H + DW_TBN - 1) / DW_TBN;
-    d.counter = a.w.counters;
+    d.counter = a.w.counters + 16;
     d.accum = (dims->flags & MOONEP_GRAD_ACCUM) ? 1 : 0;
     if (ph & MOONEP_PHASE_DW2) {
         rc = launch_dw<2>(d, s);
@@ -1351,6 +1400,6 @@ extern "C" int moonep_grouped_ffn_backward(const moonep_dims_t* dims, const void
     d.dw_home = dw13_home;
     d.dw_slot = dw13_red;
     d.ntiles_n = (2 * I + DW_TBN - 1) / DW_TBN;
-    d.counter = a.w.counters + 1;
+    d.counter = a.w.counters + 24;
     return (ph & MOONEP_PHASE_DW13) ? launch_dw<13>(d, s) : MOONEP_OK;
 }
