@@ -101,8 +101,9 @@ def test_backward_mid(B):
     _backward_check(MID.with_(B=B))
 
 
-# H and I multiples of 512: the row GEMMs may compute the tails of at most 128 rows as 128 x 512
-# tiles (a second launch); the plan must hold such tails for the case to exercise them
+# Many groups that end in a tail of at most 128 rows: row tiles that are mostly padding rows
+# (loaded as zeros), whose outputs must not be stored; the plan must hold such tails for the case
+# to exercise them
 WIDE = MID.with_(H=512, I=512, S=400, seed=6)
 
 
