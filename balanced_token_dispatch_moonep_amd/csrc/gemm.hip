@@ -882,14 +882,15 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_rows_kernel(GemmArgs a) {
 //
 // Tile order.  Each target's MT x NT tile grid is cut into eight blocks of dw_bm x dw_bn tiles
 // (the split with the fewest panels per block), one per XCD (workgroup b runs on XCD b mod 8).
-// The XCD's workgroups take its blocks, target after target, from the XCD's own counter, so
-// the tiles in flight on an XCD share dw_bm A panels and dw_bn B panels in its L2.  A tile
-// at position (i, j) of its block runs the full K steps of a one-segment target rotated by
-// 3(i + j) steps (its last, possibly partial, step stays last), so tiles that share a panel
-// read a slab some steps apart and the later reader can find it in L2 instead of waiting on
-// the same miss.  Against one global largest-first order this measured dW13 5.7% and dW2 4.4%
-// faster; a block without the rotation gained about 3.6% on dW13 and nothing on dW2, and
-// rotations of 1 to 5 steps per position measured within 1% of each other.
+// The XCD's workgroups take its blocks, target after target, from the XCD's own counter
+// (n-tiles fastest inside a block), so the tiles in flight on an XCD share a few A panels and
+// dw_bn B panels in its L2.  A tile at position (i, j) of its block runs the full K steps of a
+// one-segment target rotated by 3(i + j) steps (its last, possibly partial, step stays last),
+// so tiles that share a panel read a slab some steps apart and the later reader can find it in
+// L2 instead of waiting on the same miss.  Against one global largest-first order this
+// measured dW13 8% and dW2 5% faster; a block without the rotation gained about 3.6% on dW13
+// and nothing on dW2, m-tiles fastest 2.5% and 1% less, and rotations of 1 to 5 steps per
+// position measured within 1-2% of each other.
 // ---------------------------------------------------------------------------
 // WHICH (2 or 13) only separates the two weight-gradient launches' kernel names in traces.
 //
@@ -947,7 +948,7 @@ __global__ __launch_bounds__(DWT<TBN>::NTHR, TBN == 128 ? 2 : 1) void gemm_dw_ke
     auto setup = [&](int t, int par) {
         const int target = w.dw_order[t / per_target];
         const int local = t % per_target;
-        const int i = local % bm, j = local / bm;
+        const int j = local % bn, i = local / bn;        // n-tiles fastest
         const int mt = bx * bm + i, nt = by * bn + j;
         if (mt >= MT || nt >= NT) return false;
         rot = 3 * (i + j);
