@@ -82,6 +82,12 @@ def parse():
                         "and prints a markdown summary")
     p.add_argument("--stats-from", metavar="DIR",
                    help="no GPU work: print a markdown table of a rocprofv3 --stats kernel summary")
+    p.add_argument("--l2-from", nargs=2, metavar=("PMC_DIR1", "PMC_DIR2"),
+                   help="no GPU work: reduce two rocprofv3 --pmc runs of this bench (TCC_HIT_sum "
+                        "TCC_MISS_sum TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_LEVEL_sum, then TCC_TAG_STALL_sum "
+                        "TCC_EA0_WRREQ_sum TCC_EA0_WRREQ_LEVEL_sum TCC_EA0_RDREQ_32B_sum, each with "
+                        "--kernel-trace) to a markdown table of every GEMM kernel's L2 hit rate, reads "
+                        "beyond L2 and their mean latency")
     return p.parse_args()
 
 
@@ -124,6 +130,8 @@ def main():
         return print_stats(args.stats_from)
     if args.mfma_from:
         return write_mfma(*args.mfma_from)
+    if args.l2_from:
+        return print_l2(*args.l2_from)
     if args.steps < 1 or args.warmup < 0:
         print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
         return 2
@@ -762,6 +770,47 @@ def write_mfma(pmc_dir, bench_json):
           "traced ms | implied clock GHz |")
     print("|---|---|---:|---:|---:|---:|---:|---:|")
     print("\n".join(rows))
+    return 0
+
+
+def l2_rows(dir1, dir2):
+    """Per GEMM call: mean traced ms, L2 hit rate, reads beyond L2 (128-byte requests), their mean
+    latency (TCC_EA0_RDREQ_LEVEL / TCC_EA0_RDREQ, in L2 cycles), the writes' mean latency and the
+    tag stalls, from two rocprofv3 --pmc runs with --kernel-trace."""
+    cnt = {c: _pmc_per_dispatch(dir1 if c in ("TCC_HIT_sum", "TCC_MISS_sum", "TCC_EA0_RDREQ_sum",
+                                              "TCC_EA0_RDREQ_LEVEL_sum") else dir2, c)
+           for c in ("TCC_HIT_sum", "TCC_MISS_sum", "TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_LEVEL_sum",
+                     "TCC_TAG_STALL_sum", "TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_LEVEL_sum")}
+    dur = _kernel_durations(dir1)
+    out = []
+    for call, kname in KERNEL_NAMES.items():
+        if not call.startswith("gemm_"):
+            continue
+        k = next((n for n in cnt["TCC_HIT_sum"] if _kernel_call(n) == call), None)
+        if k is None or any(k not in cnt[c] for c in cnt):
+            continue
+        v = {c: cnt[c][k][0] for c in cnt}
+        rd, wr = v["TCC_EA0_RDREQ_sum"], v["TCC_EA0_WRREQ_sum"]
+        ms = dur.get(k, 0.0) / 1e6
+        out.append({"call": call, "kernel": kname, "ms": ms,
+                    "hit": v["TCC_HIT_sum"] / max(v["TCC_HIT_sum"] + v["TCC_MISS_sum"], 1.0),
+                    "reads": rd, "read_GB": rd * 128 / 1e9,
+                    "read_latency": v["TCC_EA0_RDREQ_LEVEL_sum"] / rd if rd else None,
+                    "write_latency": v["TCC_EA0_WRREQ_LEVEL_sum"] / wr if wr else None,
+                    "tag_stall": v["TCC_TAG_STALL_sum"]})
+    return out
+
+
+def print_l2(dir1, dir2):
+    print("| kernel | call | ms | L2 hit rate | reads beyond L2 (128 B) | rate | mean miss latency | "
+          "mean write latency | tag stalls |")
+    print("|---|---|---:|---:|---:|---:|---:|---:|---:|")
+    for r in l2_rows(dir1, dir2):
+        rate = f"{r['read_GB'] / r['ms']:.2f} TB/s" if r["ms"] else "—"
+        rl = f"{r['read_latency']:.0f} cycles" if r["read_latency"] is not None else "—"
+        wl = f"{r['write_latency']:.0f} cycles" if r["write_latency"] is not None else "—"
+        print(f"| `{r['kernel']}` | {r['call']} | {r['ms']:.2f} | {r['hit'] * 100:.0f}% | "
+              f"{r['reads']:.3g} ({r['read_GB']:.1f} GB) | {rate} | {rl} | {wl} | {r['tag_stall']:.2g} |")
     return 0
 
 

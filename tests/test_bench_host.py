@@ -70,3 +70,41 @@ def test_traffic_digest_ignores_comments_only():
     b = "// header\nint a = 1;\n/* two\n   lines */\nint b = 2;   \n"
     assert bench._code_only(a) == bench._code_only(b)
     assert bench._code_only(a) != bench._code_only("int a = 3;\nint b = 2;\n")
+
+
+def _write_pmc(d, counters, kernel, dispatches, start=1000):
+    """A rocprofv3 -f csv counter_collection + kernel_trace pair: two instances per counter (the
+    reducer sums them per dispatch), durations of 1 ms per dispatch."""
+    import csv
+    os.makedirs(d, exist_ok=True)
+    with open(os.path.join(d, "p_counter_collection.csv"), "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for i in range(dispatches):
+            for c, v in counters.items():
+                w.writerow([i, kernel, c, v / 2])
+                w.writerow([i, kernel, c, v / 2])
+    with open(os.path.join(d, "p_kernel_trace.csv"), "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        for i in range(dispatches):
+            w.writerow([i, kernel, start, start + 1_000_000])
+
+
+def test_l2_reducer_on_synthetic_counters(tmp_path):
+    """--l2-from: hit rate = hits / (hits + misses), reads in 128-byte requests, latency =
+    outstanding-request cycles / requests, per GEMM call matched by its kernel name."""
+    kernel = "void " + bench.KERNEL_NAMES["gemm_dw13"] + "(moonep::GemmArgs)"
+    d1, d2 = str(tmp_path / "p1"), str(tmp_path / "p2")
+    _write_pmc(d1, {"TCC_HIT_sum": 600.0, "TCC_MISS_sum": 400.0, "TCC_EA0_RDREQ_sum": 1e6,
+                    "TCC_EA0_RDREQ_LEVEL_sum": 7e8}, kernel, 2)
+    _write_pmc(d2, {"TCC_TAG_STALL_sum": 5.0, "TCC_EA0_WRREQ_sum": 2e6, "TCC_EA0_WRREQ_LEVEL_sum": 5e8,
+                    "TCC_EA0_RDREQ_32B_sum": 0.0}, kernel, 2)
+    rows = bench.l2_rows(d1, d2)
+    assert len(rows) == 1
+    r = rows[0]
+    assert r["call"] == "gemm_dw13" and abs(r["ms"] - 1.0) < 1e-9
+    assert abs(r["hit"] - 0.6) < 1e-12
+    assert abs(r["read_GB"] - 1e6 * 128 / 1e9) < 1e-12
+    assert abs(r["read_latency"] - 700.0) < 1e-9 and abs(r["write_latency"] - 250.0) < 1e-9
+    assert r["tag_stall"] == 5.0
