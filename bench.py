@@ -31,9 +31,9 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 SWEEP = (0.0, 0.5, 2.0, 4.0, 8.0)
 
 # timed call -> the one kernel it launches (name as in rocprofv3 kernel traces); the plan call
-# launches four small kernels and has no entry.  The weight-gradient calls also launch a
-# one-workgroup kernel that resets their eight per-XCD tile counters and orders their targets before the GEMM,
-# the row GEMM calls a one-wave counter reset and a one-wave tile prefix.
+# launches three small kernels and has no entry.  The weight-gradient calls also launch a
+# one-workgroup kernel that resets their eight per-XCD tile counters and orders their targets
+# before the GEMM, the row GEMM calls a one-wave counter reset and a one-wave tile prefix.
 KERNEL_NAMES = {
     "prefetch": "moonep::prefetch_kernel",
     "dispatch": "moonep::dispatch_kernel<false, false, 0, 2, false, true>",
