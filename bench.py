@@ -556,7 +556,7 @@ def algorithmic_work(cfg, st, cu, dst, topk):
         "gemm_dw13": (4 * mhi, Mr * H * 2 + Mr * 2 * I * 2 + (E + n_slot) * H * 2 * I * 4),
     }
     work = {
-        "plan": ("hbm", 8.0 * Mr, 8.0 * Mr, f"topk read + dest write, {Mr} pairs (4 kernels)"),
+        "plan": ("hbm", 8.0 * Mr, 8.0 * Mr, f"topk read + dest write, {Mr} pairs (3 kernels)"),
         "prefetch": ("hbm", 2.0 * n_slot * NW * 2, 2.0 * n_slot * NW * 2,
                      f"{n_slot} slot replicas x 2 x {NW} bf16 weights (read + write)"),
         "dispatch": ("hbm", xbytes + rbytes + 4.0 * Mr, xbytes + rbytes + 4.0 * Mr,
